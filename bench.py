@@ -1,0 +1,280 @@
+#!/usr/bin/env python3
+"""Benchmark of the emulated FP4 linear layer on one MI355X.
+
+One step = the whole hot path on the FFN up-projection shape
+(X 16384x4096 bf16, W 14336x4096 bf16, dY 16384x14336 bf16), as a refresh
+step of sample-and-hold tensor scaling:
+  amax(X), amax(W), amax(dY)
+  quantize X  ROW16 RNE          (fwd operand)
+  quantize W  TILE16x16 RNE + transposed copy (fwd and dgrad operand)
+  quantize dY ROW16 SR           (dgrad operand)
+  quantize dY COL16 SR           (wgrad operand, along tokens)
+  quantize X  COL16 RNE          (wgrad operand, along tokens)
+  Y  = Xq Wq^T     (bf16 out)    fwd
+  dX = dYq Wq      (bf16 out)    dgrad
+  dW = dYq^T Xq    (fp32 out)    wgrad
+value = 3 * 2 M N K flops / step time (TFLOP/s); inputs are resident in HBM
+before timing starts. Also measured in the same run: each kernel's average
+duration (HIP events on the launch stream), the quantize-only workload
+(8192x4096 bf16 ROW16 RNE, rotating over >256 MiB of inputs so the Infinity
+Cache cannot serve it) in GB/s, and the CPU oracle on a bounded sample.
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+METRIC = "FP4-emulated linear TFLOP/s (fwd+dgrad+wgrad) and quantize GB/s, % of roofline"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--kernel-reps", type=int, default=10)
+    ap.add_argument("--quiet", action="store_true")
+    return ap.parse_args()
+
+
+def log(args, *a):
+    if not args.quiet:
+        print(*a, file=sys.stderr, flush=True)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from fp4_block_scaled_fp4q_amd import api, inputs
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t0 = time.time()
+    wl = inputs.make("ffn_up_step")
+    M, N, K = wl.dims["M"], wl.dims["N"], wl.dims["K"]
+    X = wl.tensors["X"].t.to(dev)
+    W = wl.tensors["W"].t.to(dev)
+    dY = wl.tensors["dY"].t.to(dev)
+    host = wl
+    log(args, f"inputs ready in {time.time() - t0:.1f}s: M={M} N={N} K={K}")
+
+    u8 = dict(dtype=torch.uint8, device=dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    amax = {k: torch.empty(1, **f32) for k in ("X", "W", "dY")}
+    S = {k: torch.empty(1, **f32) for k in ("x", "w", "dy", "dyt", "xt")}
+    xq = api.QTensor(torch.empty((M, K // 2), **u8), torch.empty((M, K // 16), **u8), S["x"], M, K, api.ROW16)
+    wq = api.QTensor(torch.empty((N, K // 2), **u8), torch.empty((N // 16, K // 16), **u8), S["w"], N, K,
+                     api.TILE16x16)
+    wqt = api.QTensor(torch.empty((K, N // 2), **u8), torch.empty((K // 16, N // 16), **u8), S["w"], K, N,
+                      api.TILE16x16)
+    dyq = api.QTensor(torch.empty((M, N // 2), **u8), torch.empty((M, N // 16), **u8), S["dy"], M, N, api.ROW16)
+    dyqt = api.QTensor(torch.empty((N, M // 2), **u8), torch.empty((N, M // 16), **u8), S["dyt"], N, M,
+                       api.ROW16)
+    xqt = api.QTensor(torch.empty((K, M // 2), **u8), torch.empty((K, M // 16), **u8), S["xt"], K, M, api.ROW16)
+    Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    dX = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+    dW = torch.empty((N, K), **f32)
+    T = 448.0
+    seed = 0
+
+    # every launch of one step, in order, as (kernel family, callable)
+    ops = [
+        ("amax", lambda: api.fp4q_amax(X, amax["X"])),
+        ("amax", lambda: api.fp4q_amax(W, amax["W"])),
+        ("amax", lambda: api.fp4q_amax(dY, amax["dY"])),
+        ("quant_x_row16", lambda: api.fp4q_quantize(X, amax["X"], T, api.ROW16, api.RNE, 0, 0,
+                                                    xq.codes, xq.scales, S["x"])),
+        ("quant_w_tile", lambda: api.fp4q_quantize(W, amax["W"], T, api.TILE16x16, api.RNE, 0, 0,
+                                                   wq.codes, wq.scales, S["w"], wqt.codes, wqt.scales)),
+        ("quant_dy_row16_sr", lambda: api.fp4q_quantize(dY, amax["dY"], T, api.ROW16, api.SR, seed, 0,
+                                                        dyq.codes, dyq.scales, S["dy"])),
+        ("quant_dy_col16_sr", lambda: api.fp4q_quantize(dY, amax["dY"], T, api.COL16, api.SR, seed, 0,
+                                                        dyqt.codes, dyqt.scales, S["dyt"])),
+        ("quant_x_col16", lambda: api.fp4q_quantize(X, amax["X"], T, api.COL16, api.RNE, 0, 0,
+                                                    xqt.codes, xqt.scales, S["xt"])),
+        ("gemm_fwd", lambda: api.fp4q_linear_fwd(xq, wq, Y)),
+        ("gemm_dgrad", lambda: api.fp4q_linear_dgrad(dyq, wqt, dX)),
+        ("gemm_wgrad", lambda: api.fp4q_linear_wgrad(dyqt, xqt, dW)),
+    ]
+
+    def step():
+        for _, fn in ops:
+            fn()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(args, "warmup done")
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record()
+    for _ in range(args.steps):
+        step()
+    ev1.record()
+    torch.cuda.synchronize()
+    ms_per_step = ev0.elapsed_time(ev1) / args.steps
+    flops_step = 3 * 2.0 * M * N * K
+    value = flops_step / (ms_per_step * 1e-3) / 1e12
+    log(args, f"timed {args.steps} steps: {ms_per_step:.3f} ms/step, {value:.1f} TFLOP/s")
+
+    # per-kernel average durations (events bracketing kernel_reps launches)
+    kern = {}
+    for name, fn in ops:
+        if name in kern:
+            continue
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        fn()
+        a.record()
+        for _ in range(args.kernel_reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        kern[name] = a.elapsed_time(b) / args.kernel_reps * 1e3  # us per call
+    log(args, "per-call us: " + ", ".join(f"{k}={v:.1f}" for k, v in kern.items()))
+
+    gemm_us = (kern["gemm_fwd"] + kern["gemm_dgrad"] + kern["gemm_wgrad"]) / 3.0
+    gemm_tflops = 2.0 * M * N * K / (gemm_us * 1e-6) / 1e12
+
+    # algorithmic bytes of each codec launch (read once + write once)
+    def qbytes(rows, cols, es, transposed=False):
+        b = rows * cols * es + rows * cols / 2 + rows * cols / 16
+        if transposed:
+            b += rows * cols / 2 + rows * cols / 256
+        return b
+    codec_bytes = {
+        "amax": (M * K + N * K + M * N) * 2 / 3.0,  # average of the three launches
+        "quant_x_row16": qbytes(M, K, 2), "quant_w_tile": qbytes(N, K, 2, True) - N * K / 16 + N * K / 256,
+        "quant_dy_row16_sr": qbytes(M, N, 2), "quant_dy_col16_sr": qbytes(M, N, 2),
+        "quant_x_col16": qbytes(M, K, 2),
+    }
+    codec_gbs = {k: codec_bytes[k] / (kern[k] * 1e-6) / 1e9 for k in codec_bytes}
+
+    # quantize-only workload: 8192x4096 bf16 ROW16 RNE, held amax, rotated inputs
+    qw = inputs.make("quantize", with_held=True)
+    Mq, Kq = qw.dims["M"], qw.dims["K"]
+    Xq0 = qw.tensors["X"].t.to(dev)
+    held = api.amax(qw.tensors["X"].held_from.to(dev))
+    nrot = 6  # 6 x 64 MiB inputs > 256 MiB Infinity Cache
+    Xrot = [Xq0] + [Xq0.clone() for _ in range(nrot - 1)]
+    qc = torch.empty((Mq, Kq // 2), **u8)
+    qs = torch.empty((Mq, Kq // 16), **u8)
+    qS = torch.empty(1, **f32)
+    for i in range(nrot):
+        api.fp4q_quantize(Xrot[i], held, T, api.ROW16, api.RNE, 0, 0, qc, qs, qS)
+    reps = 5 * nrot
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for i in range(reps):
+        api.fp4q_quantize(Xrot[i % nrot], held, T, api.ROW16, api.RNE, 0, 0, qc, qs, qS)
+    b.record()
+    torch.cuda.synchronize()
+    q_us = a.elapsed_time(b) / reps * 1e3
+    q_bytes = Mq * Kq * (2 + 0.5 + 1 / 16)
+    q_gbs = q_bytes / (q_us * 1e-6) / 1e9
+    del Xrot
+    log(args, f"quantize-only 8192x4096: {q_us:.2f} us, {q_gbs:.0f} GB/s")
+
+    # traffic from committed rocprofv3 counters, valid only for this source
+    traffic = None
+    tf = os.path.join(ROOT, "profiles", "gemm_ffn_up_traffic.json")
+    if os.path.exists(tf):
+        try:
+            rec = json.load(open(tf))
+            src = open(os.path.join(ROOT, "fp4_block_scaled_fp4q_amd", "csrc", "gemm.hip"), "rb").read()
+            if rec.get("gemm_hip_sha256") == hashlib.sha256(src).hexdigest():
+                traffic = rec.get("bytes_per_launch")
+        except Exception:
+            traffic = None
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(args, host, M, N, K)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "ffn_up_step: fwd+dgrad+wgrad refresh step, X 16384x4096 bf16 "
+                               "(t3 outlier channels), W 14336x4096 bf16 N(0,0.02) 16x16 blocks, "
+                               "dY 16384x14336 bf16 log-uniform with SR",
+                   "M": M, "N": N, "K": K, "target": T, "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "mfma", "kernel": "gemm_kernel (fwd/dgrad/wgrad average)",
+                     "achieved": round(gemm_tflops, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(gemm_tflops / BF16_PEAK_TFLOPS, 4), "traffic": traffic},
+        "kernels_us": {k: round(v, 2) for k, v in kern.items()},
+        "codec_gbs": {k: round(v, 1) for k, v in codec_gbs.items()},
+        "quantize_only": {"workload": "8192x4096 bf16 ROW16 RNE, held amax", "us": round(q_us, 2),
+                          "GB/s": round(q_gbs, 1), "frac_hbm": round(q_gbs / HBM_PEAK_GBS, 4)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(args, wl, M, N, K):
+    """The oracle, as it stands, on a bounded sample of one step: the first
+    Ms token rows of X and dY (their ROW16/COL16 quantizations, fwd and dgrad
+    on those rows, wgrad contracting over those tokens) plus the full weight
+    quantization; value scaled to the step's FLOPs per second."""
+    import numpy as np
+
+    import oracle
+    from threadpoolctl import threadpool_info
+
+    Ms = 128
+    Xs = wl.tensors["X"].oracle_view[:Ms]
+    dYs = wl.tensors["dY"].oracle_view[:Ms]
+    Wv = wl.tensors["W"].oracle_view
+    t0 = time.perf_counter()
+    ax, aw, ady = oracle.amax(Xs), oracle.amax(Wv), oracle.amax(dYs)
+    xq = oracle.quantize(Xs, ax).q
+    w = oracle.quantize(Wv, aw, layout=oracle.TILE16, transposed=True)
+    dyq = oracle.quantize(dYs, ady, rnd=oracle.SR).q
+    dyqt = oracle.quantize(dYs, ady, layout=oracle.COL16, rnd=oracle.SR).q
+    xqt = oracle.quantize(Xs, ax, layout=oracle.COL16).q
+    t_codec = time.perf_counter() - t0
+    oracle.gemm(xq, w.q)
+    oracle.gemm(dyq, w.qt)
+    oracle.gemm(dyqt, xqt)
+    dt = time.perf_counter() - t0
+    flops = 3 * 2.0 * Ms * N * K
+    blas_threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    log(args, f"cpu oracle sample: {dt:.1f}s ({t_codec:.1f}s codec), {flops / dt / 1e12:.4f} TFLOP/s")
+    return {"value": round(flops / dt / 1e12, 5), "unit": "TFLOP/s", "cores": int(blas_threads),
+            "kind": "oracle",
+            "sample": f"first {Ms} of {M} token rows of the ffn_up_step (amax + ROW16/COL16 "
+                      f"quantize of X and dY rows, full W TILE quantize, fwd/dgrad/wgrad on those "
+                      f"rows in fp64 BLAS); codec single-threaded C, GEMMs on {blas_threads} BLAS "
+                      f"threads; {dt:.1f} s",
+            "seconds": round(dt, 2)}
+
+
+if __name__ == "__main__":
+    main()

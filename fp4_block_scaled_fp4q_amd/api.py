@@ -1,0 +1,159 @@
+"""Python face of the C ABI: the same entry points, taking torch tensors.
+
+Each ``fp4q_*`` function checks that its tensors are CUDA (HIP) tensors of
+the right dtype and layout, passes their device pointers, row strides and the
+current stream to libfp4q.so, and raises ``Fp4qError`` on a non-OK status.
+``quantize`` additionally allocates the output tensors with torch (device
+memory is torch's job here) before calling ``fp4q_quantize``.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import torch
+
+from . import _lib
+from ._lib import BF16, COL16, F32, QTensorC, RNE, ROW16, SR, TILE16x16, check, lib
+
+__all__ = ["QTensor", "fp4q_amax", "fp4q_quantize", "fp4q_dequant", "fp4q_linear_fwd",
+           "fp4q_linear_dgrad", "fp4q_linear_wgrad", "quantize", "amax", "dequant",
+           "ROW16", "COL16", "TILE16x16", "RNE", "SR", "F32", "BF16"]
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise TypeError(f"fp4q: unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+def _torch_dtype(code: int) -> torch.dtype:
+    return torch.bfloat16 if code == BF16 else torch.float32
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _dev2d(t: torch.Tensor, name: str) -> None:
+    if not t.is_cuda:
+        raise ValueError(f"fp4q: {name} must be a device tensor")
+    if t.dim() != 2 or (t.shape[1] > 1 and t.stride(1) != 1):
+        raise ValueError(f"fp4q: {name} must be 2-D with unit column stride")
+
+
+def _ptr(t: torch.Tensor | None) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+@dataclass
+class QTensor:
+    """A quantized operand on the device (see fp4q_qtensor)."""
+    codes: torch.Tensor      # uint8 [rows, cols/2]
+    scales: torch.Tensor     # uint8 [rows, cols/16] (ROW16) or [rows/16, cols/16] (TILE)
+    enc_scale: torch.Tensor  # float32 [1]: the tensor scale S
+    rows: int
+    cols: int
+    layout: int              # ROW16 or TILE16x16
+
+    def c(self) -> QTensorC:
+        return QTensorC(self.codes.data_ptr(), self.scales.data_ptr(), self.enc_scale.data_ptr(),
+                        self.rows, self.cols, self.layout)
+
+
+# ---------------------------------------------------------------- entry points
+def fp4q_amax(x: torch.Tensor, amax_out: torch.Tensor) -> None:
+    _dev2d(x, "x")
+    check("fp4q_amax", lib().fp4q_amax(x.data_ptr(), _dtype_code(x), x.shape[0], x.shape[1],
+                                       x.stride(0), amax_out.data_ptr(), _stream()))
+
+
+def fp4q_quantize(x: torch.Tensor, amax_held: torch.Tensor, target: float, layout: int, rnd: int,
+                  seed: int, subseq: int, codes: torch.Tensor, scales: torch.Tensor,
+                  enc_scale_out: torch.Tensor | None = None, codes_t: torch.Tensor | None = None,
+                  scales_t: torch.Tensor | None = None, diag: torch.Tensor | None = None) -> None:
+    _dev2d(x, "x")
+    st = lib().fp4q_quantize(x.data_ptr(), _dtype_code(x), x.shape[0], x.shape[1], x.stride(0),
+                             amax_held.data_ptr(), float(target), int(layout), int(rnd),
+                             int(seed) & (2 ** 64 - 1), int(subseq) & 0xFFFFFFFF,
+                             codes.data_ptr(), scales.data_ptr(), _ptr(enc_scale_out),
+                             _ptr(codes_t), _ptr(scales_t), _ptr(diag), _stream())
+    check("fp4q_quantize", st)
+
+
+def fp4q_dequant(q: QTensor, out: torch.Tensor) -> None:
+    qc = q.c()
+    check("fp4q_dequant", lib().fp4q_dequant(qc, out.data_ptr(), _dtype_code(out), _stream()))
+
+
+def _gemm(name: str, a: QTensor, b: QTensor, y: torch.Tensor) -> None:
+    if not y.is_contiguous():
+        raise ValueError(f"{name}: output must be contiguous")
+    if tuple(y.shape) != (a.rows, b.rows):
+        raise ValueError(f"{name}: output shape {tuple(y.shape)} != {(a.rows, b.rows)}")
+    ac, bc = a.c(), b.c()
+    check(name, getattr(lib(), name)(ac, bc, y.data_ptr(), _dtype_code(y), _stream()))
+
+
+def fp4q_linear_fwd(xq: QTensor, wq: QTensor, y: torch.Tensor) -> None:
+    """y[M, N] = Xq . Wq^T (X ROW16 [M, K], W TILE16x16 [N, K])."""
+    _gemm("fp4q_linear_fwd", xq, wq, y)
+
+
+def fp4q_linear_dgrad(dyq: QTensor, wqt: QTensor, dx: torch.Tensor) -> None:
+    """dx[M, K] = dYq . Wq (dY ROW16 [M, N], W's transposed copy [K, N])."""
+    _gemm("fp4q_linear_dgrad", dyq, wqt, dx)
+
+
+def fp4q_linear_wgrad(dyqt: QTensor, xqt: QTensor, dw: torch.Tensor) -> None:
+    """dw[N, K] = dYq^T . Xq (dY COL16 stored [N, M], X COL16 stored [K, M])."""
+    _gemm("fp4q_linear_wgrad", dyqt, xqt, dw)
+
+
+# ---------------------------------------------------------------- helpers
+def amax(x: torch.Tensor) -> torch.Tensor:
+    out = torch.empty(1, dtype=torch.float32, device=x.device)
+    fp4q_amax(x, out)
+    return out
+
+
+def quantize(x: torch.Tensor, amax_held: torch.Tensor, target: float = 448.0, layout: int = ROW16,
+             rnd: int = RNE, seed: int = 0, subseq: int = 0, transposed: bool = False,
+             with_diag: bool = False):
+    """Allocate outputs and run fp4q_quantize.
+
+    Returns (q, qt, diag): q is the operand as the GEMMs read it (for COL16,
+    the [cols, rows] transpose stored ROW16), qt the transposed TILE copy or
+    None, diag the int32[2] repair counts or None.
+    """
+    _dev2d(x, "x")
+    R, C = x.shape
+    dev = x.device
+    u8 = dict(dtype=torch.uint8, device=dev)
+    S = torch.empty(1, dtype=torch.float32, device=dev)
+    if layout == COL16:
+        codes = torch.empty((C, R // 2), **u8)
+        scales = torch.empty((C, R // 16), **u8)
+    else:
+        codes = torch.empty((R, C // 2), **u8)
+        scales = torch.empty((R, C // 16) if layout == ROW16 else (R // 16, C // 16), **u8)
+    codes_t = scales_t = None
+    if transposed:
+        codes_t = torch.empty((C, R // 2), **u8)
+        scales_t = torch.empty((C // 16, R // 16), **u8)
+    diag = torch.empty(2, dtype=torch.int32, device=dev) if with_diag else None
+    fp4q_quantize(x, amax_held, target, layout, rnd, seed, subseq, codes, scales, S,
+                  codes_t, scales_t, diag)
+    if layout == COL16:
+        q = QTensor(codes, scales, S, C, R, ROW16)
+    else:
+        q = QTensor(codes, scales, S, R, C, layout)
+    qt = QTensor(codes_t, scales_t, S, C, R, TILE16x16) if transposed else None
+    return q, qt, diag
+
+
+def dequant(q: QTensor, dtype: torch.dtype = torch.float32) -> torch.Tensor:
+    out = torch.empty((q.rows, q.cols), dtype=dtype, device=q.codes.device)
+    fp4q_dequant(q, out)
+    return out

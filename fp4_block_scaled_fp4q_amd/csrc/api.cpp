@@ -1,0 +1,176 @@
+// C ABI of libfp4q.so: argument validation (before anything is enqueued),
+// status mapping, and dispatch to the HIP kernels. No C++ exception crosses
+// this boundary and nothing here allocates.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "../../include/fp4q.h"
+#include "kernels.h"
+
+namespace {
+
+constexpr int64_t kMaxGridX = 0x7FFFFFFF / 256;  // workgroups of 256 threads
+constexpr int64_t kMaxGridY = 65535;
+
+int elem_size(int dt) { return dt == FP4Q_F32 ? 4 : (dt == FP4Q_BF16 ? 2 : 0); }
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+fp4q_status from_hip(hipError_t e) { return e == hipSuccess ? FP4Q_OK : FP4Q_E_HIP; }
+
+fp4q_status check_operand(const fp4q_qtensor* q) {
+  if (!q) return FP4Q_E_NULL;
+  if (q->rows < 0 || q->cols < 0) return FP4Q_E_SHAPE;
+  if (q->layout != FP4Q_ROW16 && q->layout != FP4Q_TILE16x16) return FP4Q_E_ARG;
+  if (q->cols % 16) return FP4Q_E_SHAPE;
+  if (q->layout == FP4Q_TILE16x16 && q->rows % 16) return FP4Q_E_SHAPE;
+  if (!q->enc_scale) return FP4Q_E_NULL;
+  if (q->rows > 0 && q->cols > 0 && (!q->codes || !q->scales)) return FP4Q_E_NULL;
+  if (!aligned(q->codes, 8)) return FP4Q_E_ALIGN;
+  return FP4Q_OK;
+}
+
+fp4q::QOperand to_operand(const fp4q_qtensor* q) {
+  fp4q::QOperand o;
+  o.codes = q->codes;
+  o.scales = q->scales;
+  o.enc_scale = q->enc_scale;
+  o.rows = q->rows;
+  o.cols = q->cols;
+  o.tile = q->layout == FP4Q_TILE16x16 ? 1 : 0;
+  return o;
+}
+
+fp4q_status gemm(const fp4q_qtensor* a, const fp4q_qtensor* b, void* y, fp4q_dtype yt,
+                 void* stream) {
+  fp4q_status st = check_operand(a);
+  if (st != FP4Q_OK) return st;
+  st = check_operand(b);
+  if (st != FP4Q_OK) return st;
+  const int es = elem_size(yt);
+  if (!es) return FP4Q_E_DTYPE;
+  if (a->cols != b->cols) return FP4Q_E_SHAPE;
+  if (a->rows > 0 && b->rows > 0 && !y) return FP4Q_E_NULL;
+  if ((b->rows + 127) / 128 > kMaxGridX || (a->rows + 127) / 128 > kMaxGridY) return FP4Q_E_SHAPE;
+  return from_hip(fp4q::launch_gemm(to_operand(a), to_operand(b), y, es,
+                                    static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+int fp4q_abi_version(void) { return FP4Q_ABI_VERSION; }
+
+const char* fp4q_status_str(fp4q_status s) {
+  switch (s) {
+    case FP4Q_OK: return "ok";
+    case FP4Q_E_NULL: return "a required pointer is NULL";
+    case FP4Q_E_SHAPE: return "invalid shape";
+    case FP4Q_E_ALIGN: return "misaligned pointer or row stride";
+    case FP4Q_E_DTYPE: return "unknown dtype";
+    case FP4Q_E_ARG: return "invalid argument";
+    case FP4Q_E_HIP: return "HIP launch error";
+  }
+  return "unknown status";
+}
+
+fp4q_status fp4q_amax(const void* x, fp4q_dtype xt, int64_t rows, int64_t cols, int64_t ld,
+                      float* amax_out, void* stream) {
+  const int es = elem_size(xt);
+  if (!es) return FP4Q_E_DTYPE;
+  if (!amax_out) return FP4Q_E_NULL;
+  if (rows < 0 || cols < 0 || ld < cols) return FP4Q_E_SHAPE;
+  if (rows > 0 && cols > 0) {
+    if (!x) return FP4Q_E_NULL;
+    if (!aligned(x, 16) || (cols * es) % 16 || (ld * es) % 16) return FP4Q_E_ALIGN;
+  }
+  if (!aligned(amax_out, 4)) return FP4Q_E_ALIGN;
+  return from_hip(fp4q::launch_amax(x, es, rows, cols, ld, amax_out,
+                                    static_cast<hipStream_t>(stream)));
+}
+
+fp4q_status fp4q_quantize(const void* x, fp4q_dtype xt, int64_t rows, int64_t cols, int64_t ld,
+                          const float* amax_held, float target, fp4q_layout layout,
+                          fp4q_round rnd, uint64_t seed, uint32_t subseq, uint8_t* codes,
+                          uint8_t* scales, float* enc_scale_out, uint8_t* codes_t,
+                          uint8_t* scales_t, int32_t* diag, void* stream) {
+  const int es = elem_size(xt);
+  if (!es) return FP4Q_E_DTYPE;
+  if (layout != FP4Q_ROW16 && layout != FP4Q_COL16 && layout != FP4Q_TILE16x16) return FP4Q_E_ARG;
+  if (rnd != FP4Q_RNE && rnd != FP4Q_SR) return FP4Q_E_ARG;
+  if (!(target > 0.0f) || !std::isfinite(target)) return FP4Q_E_ARG;
+  if ((codes_t == nullptr) != (scales_t == nullptr)) return FP4Q_E_ARG;
+  if (codes_t && layout != FP4Q_TILE16x16) return FP4Q_E_ARG;
+  if (!amax_held) return FP4Q_E_NULL;
+  if (rows < 0 || cols < 0 || ld < cols) return FP4Q_E_SHAPE;
+  if (layout != FP4Q_COL16 && cols % 16) return FP4Q_E_SHAPE;
+  if (layout != FP4Q_ROW16 && rows % 16) return FP4Q_E_SHAPE;
+  if (layout == FP4Q_COL16 && cols % 8) return FP4Q_E_ALIGN;
+  const bool nonempty = rows > 0 && cols > 0;
+  if (nonempty) {
+    if (!x || !codes || !scales) return FP4Q_E_NULL;
+    if (!aligned(x, 16) || (ld * es) % 16) return FP4Q_E_ALIGN;
+    if (!aligned(codes, 8) || (codes_t && !aligned(codes_t, 8))) return FP4Q_E_ALIGN;
+    if (layout == FP4Q_ROW16) {
+      const int64_t chunks = cols / 8;
+      const int64_t segs = (chunks + 255) / 256;
+      if (rows * segs > kMaxGridX) return FP4Q_E_SHAPE;
+    } else {
+      if ((cols / 8 + 255) / 256 > kMaxGridX || rows / 16 > kMaxGridY) return FP4Q_E_SHAPE;
+    }
+  }
+  if ((enc_scale_out && !aligned(enc_scale_out, 4)) || (diag && !aligned(diag, 4)))
+    return FP4Q_E_ALIGN;
+  fp4q::QuantArgs a;
+  a.x = x;
+  a.es = es;
+  a.rows = rows;
+  a.cols = cols;
+  a.ld = ld;
+  a.amax_held = amax_held;
+  a.target = target;
+  a.layout = (int)layout;
+  a.sr = rnd == FP4Q_SR ? 1 : 0;
+  a.seed = seed;
+  a.subseq = subseq;
+  a.codes = codes;
+  a.scales = scales;
+  a.enc_scale_out = enc_scale_out;
+  a.codes_t = codes_t;
+  a.scales_t = scales_t;
+  a.diag = diag;
+  return from_hip(fp4q::launch_quantize(a, static_cast<hipStream_t>(stream)));
+}
+
+fp4q_status fp4q_dequant(const fp4q_qtensor* q, void* out, fp4q_dtype ot, void* stream) {
+  fp4q_status st = check_operand(q);
+  if (st != FP4Q_OK) return st;
+  const int es = elem_size(ot);
+  if (!es) return FP4Q_E_DTYPE;
+  if (q->rows > 0 && q->cols > 0) {
+    if (!out) return FP4Q_E_NULL;
+    if (!aligned(out, 16)) return FP4Q_E_ALIGN;
+    if ((q->rows * (q->cols / 8) + 255) / 256 > kMaxGridX) return FP4Q_E_SHAPE;
+  }
+  return from_hip(fp4q::launch_dequant(to_operand(q), out, es, static_cast<hipStream_t>(stream)));
+}
+
+fp4q_status fp4q_linear_fwd(const fp4q_qtensor* xq, const fp4q_qtensor* wq, void* y,
+                            fp4q_dtype yt, void* stream) {
+  return gemm(xq, wq, y, yt, stream);
+}
+
+fp4q_status fp4q_linear_dgrad(const fp4q_qtensor* dyq, const fp4q_qtensor* wqt, void* dx,
+                              fp4q_dtype dxt, void* stream) {
+  return gemm(dyq, wqt, dx, dxt, stream);
+}
+
+fp4q_status fp4q_linear_wgrad(const fp4q_qtensor* dyqt, const fp4q_qtensor* xqt, void* dw,
+                              fp4q_dtype dwt, void* stream) {
+  return gemm(dyqt, xqt, dw, dwt, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,159 @@
+/*
+ * fp4q: block-scaled FP4 (E2M1 payload, UE5M3 block scale, FP32 tensor
+ * scale) quantization and the emulated FP4 linear layer, as described in
+ * "UE5M3 FP4 Block Scaling for Stable Language Model Pretraining", for AMD
+ * Instinct MI355X (gfx950). C ABI of libfp4q.so.
+ *
+ * Conventions for every entry point:
+ *  - Data pointers are DEVICE pointers (HIP memory of the current device)
+ *    unless stated otherwise; fp4q_qtensor structs themselves are read on the
+ *    host during the call. The caller allocates and owns every buffer; the
+ *    library allocates nothing and keeps no state.
+ *  - `stream` is a hipStream_t (NULL = the default stream). Work is enqueued
+ *    on it and the call returns without synchronizing. Inputs must stay valid
+ *    and outputs untouched until the stream has passed the work.
+ *  - Arguments are validated before anything is enqueued; on any error
+ *    nothing is enqueued and a status code is returned. FP4Q_E_HIP means a
+ *    launch was rejected by the runtime; faults inside kernels surface at the
+ *    caller's next synchronization, as for any HIP work.
+ *  - Inputs must be finite (the held amax may be anything: see below).
+ *  - Matrices are row-major. A quantized operand stores two 4-bit codes per
+ *    byte: element 2k of a row in bits 3:0 of byte k, element 2k+1 in bits
+ *    7:4. A code is sign (bit 3) | E2M1 magnitude (bits 2:0), magnitudes
+ *    {0, 0.5, 1, 1.5, 2, 3, 4, 6}. A scale byte is a UE5M3 code: exponent
+ *    bits 7:3 (bias 15), fraction bits 2:0; 0x01 = 2^-17 .. 0xF7 = 61440.
+ */
+#ifndef FP4Q_H
+#define FP4Q_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FP4Q_ABI_VERSION 1
+
+typedef enum {
+    FP4Q_OK = 0,
+    FP4Q_E_NULL = 1,   /* a required pointer is NULL */
+    FP4Q_E_SHAPE = 2,  /* negative size, block dimension not a multiple of 16,
+                          ld < cols, mismatched GEMM shapes, or a grid too large */
+    FP4Q_E_ALIGN = 3,  /* a pointer or row stride breaks the alignment rules */
+    FP4Q_E_DTYPE = 4,  /* unknown dtype */
+    FP4Q_E_ARG = 5,    /* unknown layout / rounding, bad target, bad buffer combination */
+    FP4Q_E_HIP = 6     /* the HIP runtime rejected a launch */
+} fp4q_status;
+
+typedef enum { FP4Q_F32 = 0, FP4Q_BF16 = 1 } fp4q_dtype;
+
+/* Payload rounding: round to nearest, ties to the even code (activations and
+ * weights, §2 and §5 of the page), or stochastic rounding with one
+ * Philox4x32-10 word per element (upstream gradients, §5.2). */
+typedef enum { FP4Q_RNE = 0, FP4Q_SR = 1 } fp4q_round;
+
+/* Block geometry (§3 and §5 of the page: 1D blocks of 16 along the
+ * contraction axis for activations and gradients, 2D 16x16 for weights). */
+typedef enum {
+    FP4Q_ROW16 = 0,     /* blocks of 16 along a row; codes [R][C/2], scales [R][C/16] */
+    FP4Q_COL16 = 1,     /* blocks of 16 down a column, stored as ROW16 of the
+                           transpose: codes [C][R/2], scales [C][R/16] */
+    FP4Q_TILE16x16 = 2  /* 16x16 tiles; codes [R][C/2], scales [R/16][C/16] */
+} fp4q_layout;
+
+/* One quantized operand as the GEMMs read it: `rows` x `cols` logical
+ * elements, contiguous along `cols` (the contraction). layout is FP4Q_ROW16
+ * (scales [rows][cols/16]; also what FP4Q_COL16 produces for the transpose)
+ * or FP4Q_TILE16x16 (scales [rows/16][cols/16]). enc_scale points to the
+ * device fp32 tensor scale S written by fp4q_quantize. codes must be 8-byte
+ * aligned. */
+typedef struct {
+    const uint8_t *codes;
+    const uint8_t *scales;
+    const float *enc_scale;
+    int64_t rows;
+    int64_t cols;
+    int32_t layout;
+} fp4q_qtensor;
+
+int fp4q_abi_version(void);
+const char *fp4q_status_str(fp4q_status s);
+
+/*
+ * Tensor amax (§5.1 of the page: each operand's tensor maximum is sampled
+ * and held). amax_out (device, one fp32) receives max |x| over the [rows,
+ * cols] tensor x of dtype xt with row stride ld elements; 0 for an empty
+ * tensor. Exact and order-independent (a maximum of sign-cleared bit
+ * patterns). x must be 16-byte aligned and cols * sizeof(elem) and
+ * ld * sizeof(elem) multiples of 16.
+ */
+fp4q_status fp4q_amax(const void *x, fp4q_dtype xt, int64_t rows, int64_t cols, int64_t ld,
+                      float *amax_out, void *stream);
+
+/*
+ * Quantize x ([rows, cols], dtype xt, row stride ld) to E2M1 codes with UE5M3
+ * block scales (§3-§5 of the page).
+ *  amax_held (device, one fp32): the held tensor amax A. The tensor scale is
+ *    S = RN(RN(6 * target) / A), S = 1 if A is 0 or not finite, and the
+ *    largest finite fp32 if the quotient overflows; target is the UE5M3
+ *    target T of §5.2 (448 default; finite and > 0). S is written to
+ *    *enc_scale_out (device, optional).
+ *  Per block: bamax = max |x|; if 0, scale code 0 and sign-only codes. Else
+ *    raw = RN(RN(bamax / 6) * S), scale = nearest UE5M3 (ties to even), with
+ *    repair: a scale rounding to 0 becomes 0x01, one rounding above 61440
+ *    becomes 0xF7 (§5.3); r = RN(S / dec); payload of x is E2M1 of RN(x * r),
+ *    saturating at 6, by RNE or SR (rnd). SR rounds |v| up to the next
+ *    magnitude iff w < ceil(p * 2^32), p its position between the two
+ *    neighbours and w = word (i mod 4) of Philox4x32-10 with key = seed and
+ *    counter (i/4 low, i/4 high, subseq, 0), i the row-major index of the
+ *    element in the logical [rows, cols] tensor (so ROW16 and COL16 of one
+ *    tensor draw the same word per element).
+ *  layout: FP4Q_ROW16 needs cols % 16 == 0; FP4Q_COL16 rows % 16 == 0 and
+ *    cols % 8 == 0; FP4Q_TILE16x16 rows % 16 == 0 and cols % 16 == 0.
+ *  codes / scales: outputs in the layout's shape (see fp4q_layout).
+ *  codes_t / scales_t: FP4Q_TILE16x16 only, both or neither: the transposed
+ *    copy (codes [cols][rows/2], scales [cols/16][rows/16]) that dgrad reads.
+ *  diag (device, optional, two int32): receives the number of blocks whose
+ *    scale was zero-rounded and saturated before repair.
+ *  Alignment: x 16-byte aligned, ld * sizeof(elem) a multiple of 16; codes
+ *    (and codes_t) 8-byte aligned.
+ */
+fp4q_status fp4q_quantize(const void *x, fp4q_dtype xt, int64_t rows, int64_t cols, int64_t ld,
+                          const float *amax_held, float target, fp4q_layout layout,
+                          fp4q_round rnd, uint64_t seed, uint32_t subseq, uint8_t *codes,
+                          uint8_t *scales, float *enc_scale_out, uint8_t *codes_t,
+                          uint8_t *scales_t, int32_t *diag, void *stream);
+
+/*
+ * Dequantize q into out ([q->rows, q->cols], row-major, dtype ot):
+ * x_hat = RN_fp32((e2m1 * dec) / S), then RNE to bf16 for FP4Q_BF16 (§6 of
+ * the page: the emulation decodes operands exactly; S is removed after).
+ * q->cols % 16 == 0; out 16-byte aligned.
+ */
+fp4q_status fp4q_dequant(const fp4q_qtensor *q, void *out, fp4q_dtype ot, void *stream);
+
+/*
+ * The emulated FP4 linear layer (§6 of the page): the contraction of the
+ * decoded operands in bf16 MFMA with fp32 accumulation, times
+ * alpha = 1 / (Sa Sb) (computed in double), rounded once to fp32 and then,
+ * for a bf16 output, once more (RNE). Outputs are row-major and contiguous.
+ *  fwd:   y[M, N]  = Xq[M, K] . Wq[N, K]^T      xq: X ROW16; wq: W TILE16x16
+ *  dgrad: dx[M, K] = dYq[M, N] . Wq[N, K]       dyq: dY ROW16 [M, N];
+ *                                               wqt: the transposed W copy [K, N]
+ *  wgrad: dw[N, K] = dYq^T[N, M] . Xq[M, K]     dyqt: dY COL16 ([N, M] stored);
+ *                                               xqt:  X COL16 ([K, M] stored)
+ * In each, both operands must have equal `cols` (the contraction length,
+ * a multiple of 16) and `rows` a multiple of 16 when their layout is TILE.
+ */
+fp4q_status fp4q_linear_fwd(const fp4q_qtensor *xq, const fp4q_qtensor *wq, void *y,
+                            fp4q_dtype yt, void *stream);
+fp4q_status fp4q_linear_dgrad(const fp4q_qtensor *dyq, const fp4q_qtensor *wqt, void *dx,
+                              fp4q_dtype dxt, void *stream);
+fp4q_status fp4q_linear_wgrad(const fp4q_qtensor *dyqt, const fp4q_qtensor *xqt, void *dw,
+                              fp4q_dtype dwt, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP4Q_H */

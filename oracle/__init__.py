@@ -77,7 +77,7 @@ def lib():
         L.oracle_quantize.restype = ctypes.c_int
         L.oracle_quantize.argtypes = [c_p, ctypes.c_int, c_i64, c_i64, c_i64, c_f, c_f,
                                       ctypes.c_int, ctypes.c_int, ctypes.c_uint64, ctypes.c_uint32,
-                                      c_p, c_p, c_p, c_p, c_p, c_p]
+                                      c_i64, c_i64, c_i64, c_p, c_p, c_p, c_p, c_p, c_p]
         L.oracle_decode_f64.restype = None
         L.oracle_decode_f64.argtypes = [c_p, c_p, c_i64, c_i64, ctypes.c_int, c_p]
         L.oracle_dequant_f32.restype = None
@@ -176,9 +176,14 @@ class Quantized:
 
 
 def quantize(x: np.ndarray, amax_held: float, T: float = 448.0, layout: int = ROW16,
-             rnd: int = RNE, seed: int = 0, subseq: int = 0, transposed: bool = False) -> Quantized:
+             rnd: int = RNE, seed: int = 0, subseq: int = 0, transposed: bool = False,
+             origin: tuple | None = None) -> Quantized:
+    """Quantize x. ``origin = (row0, col0, full_cols)`` places x inside a
+    larger logical tensor for the SR word index (default: x is the whole
+    tensor)."""
     xc, dt = _as_input(x)
     rows, cols = xc.shape
+    row0, col0, full_cols = origin if origin is not None else (0, 0, cols)
     if (layout != COL16 and cols % 16) or (layout != ROW16 and rows % 16):
         raise ValueError("the blocked dimension(s) must be multiples of 16")
     if layout == COL16:
@@ -194,7 +199,8 @@ def quantize(x: np.ndarray, amax_held: float, T: float = 448.0, layout: int = RO
     S = np.zeros(1, np.float32)
     diag = np.zeros(2, np.int32)
     rc = lib().oracle_quantize(_ptr(xc), dt, rows, cols, cols, float(amax_held), float(T), layout, rnd,
-                               int(seed), int(subseq), _ptr(codes), _ptr(scales), _ptr(S),
+                               int(seed), int(subseq), int(row0), int(col0), int(full_cols),
+                               _ptr(codes), _ptr(scales), _ptr(S),
                                _ptr(codes_t) if codes_t is not None else None,
                                _ptr(scales_t) if scales_t is not None else None, _ptr(diag))
     if rc != 0:

@@ -314,6 +314,10 @@ float oracle_tensor_scale(float amax, float T)
  *   otherwise  : raw = RN(RN(bamax / 6) * S); code = UE5M3 nearest + repair;
  *                dec = decode(code); r = RN(S / dec); v = RN(x * r);
  *                payload = E2M1 RNE or SR of v.
+ * SR words are indexed by the element's row-major position in the full
+ * logical tensor: (idx_row0 + r) * idx_cols + idx_col0 + c, so a region of a
+ * larger tensor can be quantized on its own (idx_row0 = idx_col0 = 0 and
+ * idx_cols = cols for a whole tensor).
  * diag (optional): [0] blocks zero-rounded before repair, [1] saturated.
  * ROW16 needs cols % 16 == 0, COL16 rows % 16 == 0, TILE16 both.
  * Returns 0, or -1 on a shape error.
@@ -329,6 +333,7 @@ static void put_code(uint8_t *codes, int64_t stride_bytes, int64_t row, int64_t 
 
 int oracle_quantize(const void *x, int dtype, int64_t rows, int64_t cols, int64_t ld,
                     float amax_held, float T, int layout, int rnd, uint64_t seed, uint32_t subseq,
+                    int64_t idx_row0, int64_t idx_col0, int64_t idx_cols,
                     uint8_t *codes, uint8_t *scales, float *enc_scale_out,
                     uint8_t *codes_t, uint8_t *scales_t, int32_t *diag)
 {
@@ -377,7 +382,8 @@ int oracle_quantize(const void *x, int dtype, int64_t rows, int64_t cols, int64_
                     } else {
                         float v = xv * r_mul;
                         if (rnd == ORACLE_SR)
-                            q = oracle_e2m1_encode_sr(v, neg, oracle_sr_word(seed, subseq, (uint64_t)(r * cols + c)));
+                            q = oracle_e2m1_encode_sr(v, neg, oracle_sr_word(seed, subseq,
+                                    (uint64_t)((idx_row0 + r) * idx_cols + idx_col0 + c)));
                         else
                             q = oracle_e2m1_encode_rne(v, neg);
                     }

@@ -1,0 +1,100 @@
+"""The C ABI library on a machine without a GPU: it loads, exports every
+entry point include/fp4q.h declares, and rejects bad arguments with the
+documented status codes before touching the device (no call here launches a
+kernel)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from fp4_block_scaled_fp4q_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp4q.h")
+
+FAKE = ctypes.c_void_p(0x10000)       # a 64 KiB-aligned non-null address (never dereferenced)
+FAKE_ODD = ctypes.c_void_p(0x10004)   # 4-byte aligned only
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(fp4q_\w+)\s*\(", text, re.M)))
+
+
+def test_library_exports_every_declared_function():
+    L = _lib.lib()
+    names = declared_functions()
+    assert set(names) == set(_lib.EXPORTS), names
+    for n in names:
+        assert hasattr(L, n), n
+    assert L.fp4q_abi_version() == 1
+    for s in range(7):
+        assert L.fp4q_status_str(s)
+
+
+def q(rows, cols, layout=_lib.ROW16, codes=FAKE, scales=FAKE, S=FAKE):
+    return _lib.QTensorC(codes.value if codes else None, scales.value if scales else None,
+                         S.value if S else None, rows, cols, layout)
+
+
+def quant(**kw):
+    a = dict(x=FAKE, xt=_lib.BF16, rows=32, cols=64, ld=64, amax=FAKE, target=448.0,
+             layout=_lib.ROW16, rnd=_lib.RNE, codes=FAKE, scales=FAKE, S=None, ct=None, st=None,
+             diag=None)
+    a.update(kw)
+    return _lib.lib().fp4q_quantize(a["x"], a["xt"], a["rows"], a["cols"], a["ld"], a["amax"],
+                                    a["target"], a["layout"], a["rnd"], 0, 0, a["codes"],
+                                    a["scales"], a["S"], a["ct"], a["st"], a["diag"], None)
+
+
+def test_quantize_validation():
+    assert quant(xt=5) == _lib.E_DTYPE
+    assert quant(layout=9) == _lib.E_ARG
+    assert quant(rnd=4) == _lib.E_ARG
+    assert quant(target=0.0) == _lib.E_ARG
+    assert quant(target=float("inf")) == _lib.E_ARG
+    assert quant(target=float("nan")) == _lib.E_ARG
+    assert quant(ct=FAKE) == _lib.E_ARG                       # codes_t without scales_t
+    assert quant(ct=FAKE, st=FAKE) == _lib.E_ARG              # transposed copy needs TILE
+    assert quant(amax=None) == _lib.E_NULL
+    assert quant(x=None) == _lib.E_NULL
+    assert quant(codes=None) == _lib.E_NULL
+    assert quant(cols=24, ld=24) == _lib.E_SHAPE              # ROW16 needs cols % 16
+    assert quant(rows=-1) == _lib.E_SHAPE
+    assert quant(ld=32) == _lib.E_SHAPE                       # ld < cols
+    assert quant(rows=24, layout=_lib.TILE16x16) == _lib.E_SHAPE
+    assert quant(rows=24, layout=_lib.COL16) == _lib.E_SHAPE
+    assert quant(cols=12, ld=16, layout=_lib.COL16) == _lib.E_ALIGN
+    assert quant(x=FAKE_ODD) == _lib.E_ALIGN
+    assert quant(ld=68) == _lib.E_ALIGN                       # 136-byte bf16 rows
+    assert quant(codes=FAKE_ODD) == _lib.E_ALIGN
+
+
+def test_amax_validation():
+    L = _lib.lib()
+    assert L.fp4q_amax(FAKE, 3, 16, 16, 16, FAKE, None) == _lib.E_DTYPE
+    assert L.fp4q_amax(FAKE, _lib.BF16, 16, 16, 16, None, None) == _lib.E_NULL
+    assert L.fp4q_amax(None, _lib.BF16, 16, 16, 16, FAKE, None) == _lib.E_NULL
+    assert L.fp4q_amax(FAKE, _lib.BF16, 16, 16, 8, FAKE, None) == _lib.E_SHAPE
+    assert L.fp4q_amax(FAKE, _lib.BF16, 16, 12, 16, FAKE, None) == _lib.E_ALIGN
+    assert L.fp4q_amax(FAKE_ODD, _lib.F32, 16, 16, 16, FAKE, None) == _lib.E_ALIGN
+
+
+def test_gemm_and_dequant_validation():
+    L = _lib.lib()
+    for fn in (L.fp4q_linear_fwd, L.fp4q_linear_dgrad, L.fp4q_linear_wgrad):
+        a, b = q(32, 64), q(48, 64, _lib.TILE16x16)
+        assert fn(None, b, FAKE, _lib.BF16, None) == _lib.E_NULL
+        assert fn(a, b, FAKE, 7, None) == _lib.E_DTYPE
+        assert fn(a, q(48, 80, _lib.TILE16x16), FAKE, _lib.BF16, None) == _lib.E_SHAPE
+        assert fn(a, q(40, 64, _lib.TILE16x16), FAKE, _lib.BF16, None) == _lib.E_SHAPE
+        assert fn(q(32, 72), b, FAKE, _lib.BF16, None) == _lib.E_SHAPE
+        assert fn(a, q(48, 64, 5), FAKE, _lib.BF16, None) == _lib.E_ARG
+        assert fn(a, q(48, 64, _lib.COL16), FAKE, _lib.BF16, None) == _lib.E_ARG
+        assert fn(a, b, None, _lib.BF16, None) == _lib.E_NULL
+        assert fn(q(32, 64, S=None), b, FAKE, _lib.BF16, None) == _lib.E_NULL
+        assert fn(q(32, 64, codes=FAKE_ODD), b, FAKE, _lib.BF16, None) == _lib.E_ALIGN
+    assert L.fp4q_dequant(q(32, 64), None, _lib.F32, None) == _lib.E_NULL
+    assert L.fp4q_dequant(q(32, 64), FAKE_ODD, _lib.F32, None) == _lib.E_ALIGN
+    assert L.fp4q_dequant(q(32, 64), FAKE, 9, None) == _lib.E_DTYPE

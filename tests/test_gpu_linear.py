@@ -1,0 +1,113 @@
+"""GPU parity of the emulated FP4 linear layer (fwd, dgrad, wgrad) against the
+oracle's fp64 contraction of the decoded operands: relative Frobenius error
+<= 2e-3 against the oracle rounded to the output dtype; the quantized
+operands themselves are compared bit-exactly first.
+
+Covers the tiny fp32 case (64x128x256), ragged shapes (tails in M, N and K
+that are not multiples of the 128x128x64 tile) and the bf16 workloads at
+their full sizes (8192x4096x4096 fwd and bwd; 16384x14336x4096 FFN step),
+where GEMM outputs are checked on sampled rows."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from fp4_block_scaled_fp4q_amd import api, inputs
+from parity_util import (DEV, GEMM_TOL, assert_quant_equal, dev_scalar, host_view, quant_both,
+                         rel_fro, round_out)
+
+pytestmark = pytest.mark.gpu
+
+
+def _gemm_check(y_dev: torch.Tensor, ref: np.ndarray, rows=None):
+    y = y_dev.float().cpu().numpy() if rows is None else y_dev[rows].float().cpu().numpy()
+    err = rel_fro(y, round_out(ref, y_dev.dtype))
+    assert err <= GEMM_TOL, err
+    return err
+
+
+def test_tiny_fwd_fp32():
+    wl = inputs.make("tiny_fwd")
+    X, W = wl.tensors["X"].t, wl.tensors["W"].t
+    ax = float(oracle.amax(host_view(X)))
+    aw = float(oracle.amax(host_view(W)))
+    gx, ox = quant_both(X, ax, "row16")
+    gw, ow = quant_both(W, aw, "tile", transposed=True)
+    assert_quant_equal(gx, ox)
+    assert_quant_equal(gw, ow)
+    y = torch.empty((64, 128), dtype=torch.float32, device=DEV)
+    api.fp4q_linear_fwd(gx["q"], gw["q"], y)
+    ref = oracle.gemm(ox.q, ow.q)
+    err = _gemm_check(y, ref)
+    assert err < 1e-6  # fp32 output of a short fp32-accumulated sum
+
+
+@pytest.mark.parametrize("M,N,K", [(100, 48, 80), (130, 144, 1040), (1, 16, 16), (256, 256, 4096),
+                                   (129, 272, 208), (0, 16, 32), (16, 16, 0)])
+@pytest.mark.parametrize("btile", [False, True])
+@pytest.mark.parametrize("out", [torch.float32, torch.bfloat16])
+def test_gemm_shapes(M, N, K, btile, out):
+    rng = np.random.default_rng(M * 7 + N * 3 + K)
+    A = torch.from_numpy(inputs.activation(rng, M, K, inputs.outlier_columns(rng, K)) if M and K
+                         else np.zeros((M, K), np.float32))
+    B = torch.from_numpy(inputs.gaussian(rng, N, K, 0.02) if K else np.zeros((N, K), np.float32))
+    aa = float(oracle.amax(host_view(A))) if A.numel() else 1.0
+    ab = float(oracle.amax(host_view(B))) if B.numel() else 1.0
+    ga, oa = quant_both(A, aa, "row16")
+    gb, ob = quant_both(B, ab, "tile" if btile else "row16")
+    y = torch.full((M, N), float("nan"), dtype=out, device=DEV)
+    api.fp4q_linear_fwd(ga["q"], gb["q"], y)
+    torch.cuda.synchronize()
+    if M and N:
+        if K == 0:
+            assert torch.all(y == 0)
+        else:
+            _gemm_check(y, oracle.gemm(oa.q, ob.q))
+
+
+def test_linear_small_fwd_dgrad_wgrad():
+    rng = np.random.default_rng(11)
+    M, N, K = 272, 192, 320
+    X = inputs.to_bf16(inputs.activation(rng, M, K, inputs.outlier_columns(rng, K)))
+    W = inputs.to_bf16(inputs.gaussian(rng, N, K, 0.02))
+    dY = inputs.to_bf16(inputs.loguniform_grad(rng, M, N))
+    ax, aw, ady = (float(oracle.amax(host_view(t))) for t in (X, W, dY))
+    gx, ox = quant_both(X, ax, "row16")
+    gw, ow = quant_both(W, aw, "tile", transposed=True)
+    gdy, ody = quant_both(dY, ady, "row16", rnd=1, seed=5)
+    gdyt, odyt = quant_both(dY, ady, "col16", rnd=1, seed=5)
+    gxt, oxt = quant_both(X, ax, "col16")
+    for g, o in ((gx, ox), (gw, ow), (gdy, ody), (gdyt, odyt), (gxt, oxt)):
+        assert_quant_equal(g, o)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+    dx = torch.empty((M, K), dtype=torch.bfloat16, device=DEV)
+    dw = torch.empty((N, K), dtype=torch.float32, device=DEV)
+    api.fp4q_linear_fwd(gx["q"], gw["q"], y)
+    api.fp4q_linear_dgrad(gdy["q"], gw["qt"], dx)
+    api.fp4q_linear_wgrad(gdyt["q"], gxt["q"], dw)
+    _gemm_check(y, oracle.gemm(ox.q, ow.q))
+    _gemm_check(dx, oracle.gemm(ody.q, ow.qt))
+    _gemm_check(dw, oracle.gemm(odyt.q, oxt.q))
+
+
+def _rows(q: oracle.QTensor, idx):
+    """The operand restricted to some rows (ROW16 layout only)."""
+    return oracle.QTensor(q.codes[idx], q.scales[idx], q.S, len(idx), q.cols, q.layout)
+
+
+def test_gemm_deterministic_and_launch_independent():
+    rng = np.random.default_rng(12)
+    A = torch.from_numpy(inputs.activation(rng, 512, 1024, inputs.outlier_columns(rng, 1024))).to(DEV)
+    B = torch.from_numpy(inputs.gaussian(rng, 384, 1024, 0.02)).to(DEV)
+    qa = api.quantize(A, api.amax(A))[0]
+    qb = api.quantize(B, api.amax(B), layout=api.TILE16x16)[0]
+    y1 = torch.empty((512, 384), device=DEV)
+    y2 = torch.empty((512, 384), device=DEV)
+    api.fp4q_linear_fwd(qa, qb, y1)
+    api.fp4q_linear_fwd(qa, qb, y2)
+    assert torch.equal(y1, y2)
+    # a row-slice of A gives the same rows of Y (tile position does not matter)
+    sub = api.QTensor(qa.codes[128:256], qa.scales[128:256], qa.enc_scale, 128, 1024, api.ROW16)
+    y3 = torch.empty((128, 384), device=DEV)
+    api.fp4q_linear_fwd(sub, qb, y3)
+    assert torch.equal(y3, y1[128:256])

@@ -112,3 +112,18 @@ def test_sr_seed_changes_codes():
     c = oracle.quantize(x, 6.0, rnd=oracle.SR, seed=1, subseq=1).q
     assert not np.array_equal(a.codes, b.codes)
     assert not np.array_equal(a.codes, c.codes)
+
+
+def test_sr_region_origin_matches_whole_tensor():
+    rng = np.random.default_rng(8)
+    x = (10.0 ** rng.uniform(-8, -2, (64, 64)) * rng.choice([-1, 1], (64, 64))).astype(np.float32)
+    a = oracle.amax(x)
+    whole = oracle.quantize(x, a, rnd=oracle.SR, seed=3, subseq=1).q
+    part = oracle.quantize(np.ascontiguousarray(x[16:48, 32:64]), a, rnd=oracle.SR, seed=3,
+                           subseq=1, origin=(16, 32, 64)).q
+    assert np.array_equal(part.codes, whole.codes[16:48, 16:32])
+    assert np.array_equal(part.scales, whole.scales[16:48, 2:4])
+    colw = oracle.quantize(x, a, rnd=oracle.SR, seed=3, layout=oracle.COL16).q
+    colp = oracle.quantize(np.ascontiguousarray(x[16:48, 8:24]), a, rnd=oracle.SR, seed=3,
+                           layout=oracle.COL16, origin=(16, 8, 64)).q
+    assert np.array_equal(colp.codes, colw.codes[8:24, 8:24])

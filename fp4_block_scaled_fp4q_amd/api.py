@@ -39,8 +39,13 @@ def _stream() -> int:
 def _dev2d(t: torch.Tensor, name: str) -> None:
     if not t.is_cuda:
         raise ValueError(f"fp4q: {name} must be a device tensor")
-    if t.dim() != 2 or (t.shape[1] > 1 and t.stride(1) != 1):
+    if t.dim() != 2 or (t.numel() > 0 and t.shape[1] > 1 and t.stride(1) != 1):
         raise ValueError(f"fp4q: {name} must be 2-D with unit column stride")
+
+
+def _ld(t: torch.Tensor) -> int:
+    """Row stride in elements (an empty tensor's strides are arbitrary)."""
+    return t.stride(0) if t.numel() > 0 else t.shape[1]
 
 
 def _ptr(t: torch.Tensor | None) -> int | None:
@@ -66,7 +71,7 @@ class QTensor:
 def fp4q_amax(x: torch.Tensor, amax_out: torch.Tensor) -> None:
     _dev2d(x, "x")
     check("fp4q_amax", lib().fp4q_amax(x.data_ptr(), _dtype_code(x), x.shape[0], x.shape[1],
-                                       x.stride(0), amax_out.data_ptr(), _stream()))
+                                       _ld(x), amax_out.data_ptr(), _stream()))
 
 
 def fp4q_quantize(x: torch.Tensor, amax_held: torch.Tensor, target: float, layout: int, rnd: int,
@@ -74,7 +79,7 @@ def fp4q_quantize(x: torch.Tensor, amax_held: torch.Tensor, target: float, layou
                   enc_scale_out: torch.Tensor | None = None, codes_t: torch.Tensor | None = None,
                   scales_t: torch.Tensor | None = None, diag: torch.Tensor | None = None) -> None:
     _dev2d(x, "x")
-    st = lib().fp4q_quantize(x.data_ptr(), _dtype_code(x), x.shape[0], x.shape[1], x.stride(0),
+    st = lib().fp4q_quantize(x.data_ptr(), _dtype_code(x), x.shape[0], x.shape[1], _ld(x),
                              amax_held.data_ptr(), float(target), int(layout), int(rnd),
                              int(seed) & (2 ** 64 - 1), int(subseq) & 0xFFFFFFFF,
                              codes.data_ptr(), scales.data_ptr(), _ptr(enc_scale_out),

@@ -5,9 +5,26 @@
 //
 // Each decoded element e2m1 * dec has at most 6 significant bits and lies in
 // [2^-18, 368640], so it is exact in bf16; the contraction runs on bf16 MFMA
-// (v_mfma_f32_32x32x16_bf16) with fp32 accumulation. FP4 codes and scales
-// are read from HBM (4.5 bits per element), decoded once per workgroup into
-// LDS as bf16, and consumed from LDS by the MFMA fragments.
+// (v_mfma_f32_32x32x16_bf16) with fp32 accumulation.
+//
+// Design (gfx950):
+//  * A workgroup of 4 waves owns a 256 x 256 output tile; each wave a
+//    128 x 128 sub-tile (16 MFMA accumulators of 32 x 32).
+//  * K advances in tiles of 64. FP4 codes (0.5 B/element) and one scale byte
+//    per 16 elements are read from global memory one tile ahead into
+//    registers; every thread decodes one row of A and one row of B (64
+//    elements each) to bf16 and stores them in LDS, double buffered, while
+//    the MFMAs consume the other buffer. Decoding once per workgroup costs
+//    (256 + 256) * 64 elements per 256 * 256 * 64 MACs.
+//  * Decode: v_cvt_scalef32_pk_f32_fp4 (scale 1.0) gives two exact E2M1
+//    values in fp32, one multiply each by the block's UE5M3 value (exact),
+//    and v_cvt_pk_bf16_f32 packs the exact products.
+//  * LDS rows are 8 chunks of 16 bytes (8 k each); chunk c of row r lives at
+//    slot c ^ (r & 7), so fragment reads (32 rows, one chunk) and the
+//    row-wise decode writes are both free of bank conflicts.
+//  * Workgroups are numbered so that consecutive ones on one XCD (hardware
+//    dispatch is round-robin over the 8 XCDs) cover a compact group of tiles,
+//    which keeps their shared A and B rows in that XCD's L2.
 //
 // One kernel serves fwd (A = X, ROW16; B = W, TILE), dgrad (A = dY, ROW16;
 // B = W^T, TILE) and wgrad (A = dY^T, B = X^T, both quantized along tokens):
@@ -19,139 +36,247 @@ namespace fp4q {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int BM = 128;
-constexpr int BN = 128;
+constexpr int BM = 256;
+constexpr int BN = 256;
 constexpr int BK = 64;
 constexpr int kThreads = 256;
+constexpr int kChunks = BK / 8;              // 16-byte chunks per LDS row
+constexpr int kTileChunks = BM * kChunks;    // per operand per buffer
+constexpr int kGroupM = 8;                   // M-tiles per scheduling group
 
-// Decode 8 packed codes of one block into 8 bf16 (exact), element order kept.
-// A half with bit pattern m << 9 equals e2m1(m) * 2^-14 for every magnitude
-// m (E2M1's subnormal 0.5 lines up with the half subnormals), so
-// e2m1 * dec = half(m << 9) * (dec * 2^14), one exact fp32 product.
-__device__ __forceinline__ uint4 decode8(uint32_t d, float dec14) {
-  uint32_t h[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const uint32_t q = (d >> (4 * e)) & 0xFu;
-    const float f = half_bits_to_float((q & 7u) << 9) * dec14;
-    h[e] = (f2u(f) >> 16) | ((q & 8u) << 12);
-  }
-  return make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
-}
-
-struct Stage {
-  uint2 c[2];      // codes of two 16-element blocks (8 bytes each)
-  uint32_t s[2];   // their scale codes
+// Codes and scales of one 64-element row segment (4 blocks of 16).
+struct RowSeg {
+  uint4 c0, c1;    // 32 bytes of codes
+  uint32_t s;      // 4 scale bytes, block j in bits 8j+7:8j
 };
 
-// Loader: thread t owns row (t >> 1) of the 128-row tile and k range
-// 32 * (t & 1) .. +31 of the 64-wide k tile: two blocks of 16.
-__device__ __forceinline__ Stage load_stage(const uint8_t* __restrict__ codes,
-                                            const uint8_t* __restrict__ scales, int64_t rows,
-                                            int64_t K, int tile_shift, int64_t r, int64_t k) {
-  Stage st;
+// K % 64 == 0: a whole segment is in bounds; rows past the end are clamped
+// to the last row (their products only reach outputs that are not stored),
+// so the load is branch-free.
+__device__ __forceinline__ RowSeg load_seg_full(const uint8_t* __restrict__ codes,
+                                                const uint8_t* __restrict__ scales, int64_t rows,
+                                                int64_t K, int tile_shift, int64_t r, int64_t k0) {
+  r = r < rows ? r : rows - 1;
+  const uint8_t* cp = codes + r * (K / 2) + k0 / 2;
+  const uint8_t* sp = scales + (r >> tile_shift) * (K / 16) + k0 / 16;
+  RowSeg g;
+  g.c0 = *reinterpret_cast<const uint4*>(cp);
+  g.c1 = *reinterpret_cast<const uint4*>(cp + 16);
+  g.s = *reinterpret_cast<const uint32_t*>(sp);
+  return g;
+}
+
+// General K (a multiple of 16): blocks at or beyond K read as zero codes.
+__device__ __forceinline__ RowSeg load_seg_tail(const uint8_t* __restrict__ codes,
+                                                const uint8_t* __restrict__ scales, int64_t rows,
+                                                int64_t K, int tile_shift, int64_t r, int64_t k0) {
+  r = r < rows ? r : rows - 1;
+  const uint8_t* cp = codes + r * (K / 2);
+  const uint8_t* sp = scales + (r >> tile_shift) * (K / 16);
+  uint2 b[4];
+  uint32_t s = 0u;
 #pragma unroll
-  for (int b = 0; b < 2; ++b) {
-    const int64_t kb = k + 16 * b;
-    if (r < rows && kb < K) {
-      st.c[b] = *reinterpret_cast<const uint2*>(codes + r * (K / 2) + kb / 2);
-      st.s[b] = scales[(r >> tile_shift) * (K / 16) + kb / 16];
+  for (int j = 0; j < 4; ++j) {
+    const int64_t kb = k0 + 16 * j;
+    if (kb < K) {
+      b[j] = *reinterpret_cast<const uint2*>(cp + kb / 2);
+      s |= (uint32_t)sp[kb / 16] << (8 * j);
     } else {
-      st.c[b] = make_uint2(0u, 0u);
-      st.s[b] = 0u;
+      b[j] = make_uint2(0u, 0u);
     }
   }
-  return st;
+  RowSeg g;
+  g.c0 = make_uint4(b[0].x, b[0].y, b[1].x, b[1].y);
+  g.c1 = make_uint4(b[2].x, b[2].y, b[3].x, b[3].y);
+  g.s = s;
+  return g;
 }
 
-__device__ __forceinline__ void store_stage(uint4* lds, const Stage& st, int row, int half) {
-#pragma unroll
-  for (int b = 0; b < 2; ++b) {
-    const float dec14 = ue5m3_value(st.s[b]) * 16384.0f;
-    const uint4 lo = decode8(st.c[b].x, dec14);
-    const uint4 hi = decode8(st.c[b].y, dec14);
-    const int c0 = half * 4 + 2 * b;  // 16-byte chunk index (8 k each) in the row
-    lds[row * 8 + ((c0) ^ (row & 7))] = lo;
-    lds[row * 8 + ((c0 + 1) ^ (row & 7))] = hi;
+template <bool kFullK>
+__device__ __forceinline__ RowSeg load_seg(const uint8_t* __restrict__ codes,
+                                           const uint8_t* __restrict__ scales, int64_t rows,
+                                           int64_t K, int tile_shift, int64_t r, int64_t k0) {
+  return kFullK ? load_seg_full(codes, scales, rows, K, tile_shift, r, k0)
+                : load_seg_tail(codes, scales, rows, K, tile_shift, r, k0);
+}
+
+// 8 codes (one 32-bit word, element e in bits 4e+3:4e) of a block with
+// decoded scale dec -> 8 bf16, element order kept.
+__device__ __forceinline__ uint4 decode8(uint32_t w, float dec) {
+  const f32x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+  const f32x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+  const f32x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+  const f32x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+  const bf16x2 b0 = {(__bf16)(p0.x * dec), (__bf16)(p0.y * dec)};
+  const bf16x2 b1 = {(__bf16)(p1.x * dec), (__bf16)(p1.y * dec)};
+  const bf16x2 b2 = {(__bf16)(p2.x * dec), (__bf16)(p2.y * dec)};
+  const bf16x2 b3 = {(__bf16)(p3.x * dec), (__bf16)(p3.y * dec)};
+  return make_uint4(__builtin_bit_cast(uint32_t, b0), __builtin_bit_cast(uint32_t, b1),
+                    __builtin_bit_cast(uint32_t, b2), __builtin_bit_cast(uint32_t, b3));
+}
+
+__device__ __forceinline__ uint32_t seg_word(const RowSeg& g, int c) {
+  switch (c) {
+    case 0: return g.c0.x;
+    case 1: return g.c0.y;
+    case 2: return g.c0.z;
+    case 3: return g.c0.w;
+    case 4: return g.c1.x;
+    case 5: return g.c1.y;
+    case 6: return g.c1.z;
+    default: return g.c1.w;
   }
 }
 
+// Decode block j (chunks 2j, 2j+1) of a row segment into LDS row `row`.
+__device__ __forceinline__ void store_block(uint4* __restrict__ lds, const RowSeg& g, int row, int j) {
+  uint4* base = lds + row * kChunks;
+  const int sw = row & 7;
+  const float dec = ue5m3_value((g.s >> (8 * j)) & 0xFFu);
+  base[(2 * j) ^ sw] = decode8(seg_word(g, 2 * j), dec);
+  base[(2 * j + 1) ^ sw] = decode8(seg_word(g, 2 * j + 1), dec);
+}
+
+template <bool kFullK, bool kF32Out>
 __global__ __launch_bounds__(kThreads) void gemm_kernel(
     const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales, int a_shift,
     const float* __restrict__ a_S, const uint8_t* __restrict__ b_codes,
     const uint8_t* __restrict__ b_scales, int b_shift, const float* __restrict__ b_S, int64_t M,
-    int64_t N, int64_t K, void* __restrict__ y, int y_es) {
-  __shared__ uint4 As[BM * BK / 8];
-  __shared__ uint4 Bs[BN * BK / 8];
+    int64_t N, int64_t K, int tiles_m, int tiles_n, void* __restrict__ y) {
+  // 2 buffers x (A tile + B tile) = 128 KiB
+  extern __shared__ uint4 lds[];
+
+  // ---- XCD-aware tile order: hardware dispatch sends workgroup L to XCD
+  // L % 8; give each XCD a contiguous range of the grouped tile order.
+  const int ntiles = tiles_m * tiles_n;
+  const int L = blockIdx.x;
+  const int per_xcd = (ntiles + 7) / 8;
+  const int xcd = L % 8;
+  const int local = L / 8;
+  const int full_xcds = ntiles % 8 ? ntiles % 8 : 8;  // XCDs that receive per_xcd tiles
+  const int t = xcd < full_xcds ? xcd * per_xcd + local
+                                : full_xcds * per_xcd + (xcd - full_xcds) * (per_xcd - 1) + local;
+  // grouped order: kGroupM M-tiles per group, N-tiles column by column
+  const int group = t / (kGroupM * tiles_n);
+  const int first_m = group * kGroupM;
+  const int gm = min(tiles_m - first_m, kGroupM);
+  const int in_group = t - group * kGroupM * tiles_n;
+  const int tm = first_m + in_group % gm;
+  const int tn = in_group / gm;
+
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int wm = wave >> 1;
   const int wn = wave & 1;
-  const int64_t m0 = (int64_t)blockIdx.y * BM;
-  const int64_t n0 = (int64_t)blockIdx.x * BN;
-  const int lrow = tid >> 1;
-  const int lhalf = tid & 1;
+  const int64_t m0 = (int64_t)tm * BM;
+  const int64_t n0 = (int64_t)tn * BN;
 
-  f32x16 acc[2][2];
+  f32x16 acc[4][4];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-  Stage sa = load_stage(a_codes, a_scales, M, K, a_shift, m0 + lrow, 32 * lhalf);
-  Stage sb = load_stage(b_codes, b_scales, N, K, b_shift, n0 + lrow, 32 * lhalf);
-  for (int64_t k0 = 0; k0 < K; k0 += BK) {
-    store_stage(As, sa, lrow, lhalf);
-    store_stage(Bs, sb, lrow, lhalf);
-    __syncthreads();
-    if (k0 + BK < K) {
-      sa = load_stage(a_codes, a_scales, M, K, a_shift, m0 + lrow, k0 + BK + 32 * lhalf);
-      sb = load_stage(b_codes, b_scales, N, K, b_shift, n0 + lrow, k0 + BK + 32 * lhalf);
+  const int nk = (int)((K + BK - 1) / BK);
+  RowSeg ga, gb;  // codes of tile kt + 1, decoded during iteration kt
+  if (nk > 0) {
+    ga = load_seg<kFullK>(a_codes, a_scales, M, K, a_shift, m0 + tid, 0);
+    gb = load_seg<kFullK>(b_codes, b_scales, N, K, b_shift, n0 + tid, 0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      store_block(lds, ga, tid, j);
+      store_block(lds + kTileChunks, gb, tid, j);
     }
-#pragma unroll
-    for (int s = 0; s < BK / 16; ++s) {
-      bf16x8 af[2], bfr[2];
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const int ar = wm * 64 + t * 32 + (lane & 31);
-        const int br = wn * 64 + t * 32 + (lane & 31);
-        const int ch = 2 * s + (lane >> 5);
-        af[t] = __builtin_bit_cast(bf16x8, As[ar * 8 + (ch ^ (ar & 7))]);
-        bfr[t] = __builtin_bit_cast(bf16x8, Bs[br * 8 + (ch ^ (br & 7))]);
-      }
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-    }
+    const int64_t k1 = (int64_t)min(1, nk - 1) * BK;
+    ga = load_seg<kFullK>(a_codes, a_scales, M, K, a_shift, m0 + tid, k1);
+    gb = load_seg<kFullK>(b_codes, b_scales, N, K, b_shift, n0 + tid, k1);
     __syncthreads();
   }
 
-  const double alpha = 1.0 / ((double)*a_S * (double)*b_S);
+  // lane's fragment rows inside the tile and their swizzle
+  const int arow0 = wm * 128 + (lane & 31);
+  const int brow0 = wn * 128 + (lane & 31);
+  const int hi = lane >> 5;
+
+  // fragment loads of one k16 step (A and B: 4 sub-tiles of 32 rows each)
+  auto load_frags = [&](const uint4* As, const uint4* Bs, int s, bf16x8* af, bf16x8* bfr) {
+    const int ch = 2 * s + hi;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+    for (int t4 = 0; t4 < 4; ++t4) {
+      const int ar = arow0 + t4 * 32;
+      const int br = brow0 + t4 * 32;
+      af[t4] = __builtin_bit_cast(bf16x8, As[ar * kChunks + (ch ^ (ar & 7))]);
+      bfr[t4] = __builtin_bit_cast(bf16x8, Bs[br * kChunks + (ch ^ (br & 7))]);
+    }
+  };
+
+  for (int kt = 0; kt < nk; ++kt) {
+    const uint4* As = lds + (kt & 1) * 2 * kTileChunks;
+    const uint4* Bs = As + kTileChunks;
+    uint4* An = lds + ((kt + 1) & 1) * 2 * kTileChunks;
+    // codes of tile kt + 2 (the last tile again near the end: harmless)
+    const int64_t k2 = (int64_t)min(kt + 2, nk - 1) * BK;
+    const RowSeg na = load_seg<kFullK>(a_codes, a_scales, M, K, a_shift, m0 + tid, k2);
+    const RowSeg nb = load_seg<kFullK>(b_codes, b_scales, N, K, b_shift, n0 + tid, k2);
+    bf16x8 af[2][4], bfr[2][4];
+    load_frags(As, Bs, 0, af[0], bfr[0]);
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int s = 0; s < BK / 16; ++s) {
+      const int cur = s & 1;
+      if (s + 1 < BK / 16) load_frags(As, Bs, s + 1, af[cur ^ 1], bfr[cur ^ 1]);
+      // block s of the next tile (this thread's A row and B row) is decoded
+      // in four pieces, each after four MFMAs, so that the VALU work issues
+      // while the matrix core is busy
+      const float deca = ue5m3_value((ga.s >> (8 * s)) & 0xFFu);
+      const float decb = ue5m3_value((gb.s >> (8 * s)) & 0xFFu);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[q][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][q], bfr[cur][j], acc[q][j], 0, 0, 0);
+        const bool is_a = q < 2;
+        const RowSeg& g = is_a ? ga : gb;
+        uint4* dst = (is_a ? An : An + kTileChunks) + tid * kChunks;
+        const int c = 2 * s + (q & 1);
+        dst[c ^ (tid & 7)] = decode8(seg_word(g, c), is_a ? deca : decb);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    ga = na;
+    gb = nb;
+    __syncthreads();
+  }
+
+  // epilogue: y = acc * alpha, alpha = 1 / (Sa Sb)
+  const double alpha_d = 1.0 / ((double)*a_S * (double)*b_S);
+  const float alpha = (float)alpha_d;
+  const bool alpha_normal = alpha >= 1.17549435e-38f && alpha <= 3.40282347e+38f;
+  const bool full_tile = m0 + BM <= M && n0 + BN <= N;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t c = n0 + wn * 128 + j * 32 + (lane & 31);
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int64_t r = m0 + wm * 64 + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-        const int64_t c = n0 + wn * 64 + j * 32 + (lane & 31);
-        if (r < M && c < N) {
-          const float v = (float)((double)acc[i][j][e] * alpha);
-          if (y_es == 4) {
+        const int64_t r = m0 + wm * 128 + i * 32 + 8 * (e >> 2) + 4 * hi + (e & 3);
+        const float v = alpha_normal ? acc[i][j][e] * alpha : (float)((double)acc[i][j][e] * alpha_d);
+        if (full_tile || (r < M && c < N)) {
+          if (kF32Out) {
             static_cast<float*>(y)[r * N + c] = v;
           } else {
-            const uint32_t u = f2u(v);
-            static_cast<uint16_t*>(y)[r * N + c] = (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+            static_cast<__bf16*>(y)[r * N + c] = (__bf16)v;
           }
         }
       }
+    }
 }
 
 }  // namespace
@@ -159,9 +284,30 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
 hipError_t launch_gemm(const QOperand& a, const QOperand& b, void* y, int y_es, hipStream_t s) {
   const int64_t M = a.rows, N = b.rows, K = a.cols;
   if (M == 0 || N == 0) return hipSuccess;
-  const dim3 grid((uint32_t)((N + BN - 1) / BN), (uint32_t)((M + BM - 1) / BM));
-  hipLaunchKernelGGL(gemm_kernel, grid, dim3(kThreads), 0, s, a.codes, a.scales, a.tile ? 4 : 0,
-                     a.enc_scale, b.codes, b.scales, b.tile ? 4 : 0, b.enc_scale, M, N, K, y, y_es);
+  const int tiles_m = (int)((M + BM - 1) / BM);
+  const int tiles_n = (int)((N + BN - 1) / BN);
+  const size_t lds_bytes = 2 * 2 * kTileChunks * sizeof(uint4);
+  const bool full_k = K % BK == 0;
+  const void* fn;
+  if (full_k)
+    fn = y_es == 4 ? (const void*)gemm_kernel<true, true> : (const void*)gemm_kernel<true, false>;
+  else
+    fn = y_es == 4 ? (const void*)gemm_kernel<false, true> : (const void*)gemm_kernel<false, false>;
+  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);
+  if (e != hipSuccess) return e;
+  const dim3 grid((uint32_t)(tiles_m * tiles_n)), block(kThreads);
+#define FP4Q_GEMM(FK, F32)                                                                        \
+  hipLaunchKernelGGL((gemm_kernel<FK, F32>), grid, block, lds_bytes, s, a.codes, a.scales,        \
+                     a.tile ? 4 : 0, a.enc_scale, b.codes, b.scales, b.tile ? 4 : 0, b.enc_scale, \
+                     M, N, K, tiles_m, tiles_n, y)
+  if (full_k) {
+    if (y_es == 4) FP4Q_GEMM(true, true);
+    else FP4Q_GEMM(true, false);
+  } else {
+    if (y_es == 4) FP4Q_GEMM(false, true);
+    else FP4Q_GEMM(false, false);
+  }
+#undef FP4Q_GEMM
   return hipGetLastError();
 }
 

@@ -45,6 +45,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernel-reps", type=int, default=10)
     ap.add_argument("--quiet", action="store_true")
+    ap.add_argument("--profile-op", default=None,
+                    help="profiling mode: run only this launch of the step (e.g. gemm_fwd, "
+                         "quant_x_row16, quantize_only, copy) --reps times and exit")
+    ap.add_argument("--reps", type=int, default=5)
     return ap.parse_args()
 
 
@@ -118,6 +122,10 @@ def main():
     def step():
         for _, fn in ops:
             fn()
+
+    if args.profile_op:
+        profile_only(args, ops, X, dev, api, inputs, torch)
+        return
 
     for _ in range(args.warmup):
         step()
@@ -236,6 +244,47 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+def profile_only(args, ops, X, dev, api, inputs, torch):
+    """Run each launch kind of a comma-separated --profile-op list --reps
+    times (after one untimed call), for counter collection and tuning.
+    'quantize_only' is the 8192x4096 ROW16 RNE workload; 'copy' is a plain
+    device copy of 256 MiB, the reference for scaling FETCH_SIZE and
+    WRITE_SIZE to bytes."""
+    prepared = False
+    for name in args.profile_op.split(","):
+        if name == "copy":
+            src = torch.empty(256 * 2 ** 20 // 4, dtype=torch.float32, device=dev)
+            dst = torch.empty_like(src)
+            src.fill_(1.0)
+            fn = lambda: dst.copy_(src)  # noqa: E731
+        elif name == "quantize_only":
+            qw = inputs.make("quantize", with_held=False)
+            Xq = qw.tensors["X"].t.to(dev)
+            held = api.amax(Xq)
+            u8 = dict(dtype=torch.uint8, device=dev)
+            qc = torch.empty((Xq.shape[0], Xq.shape[1] // 2), **u8)
+            qs = torch.empty((Xq.shape[0], Xq.shape[1] // 16), **u8)
+            qS = torch.empty(1, dtype=torch.float32, device=dev)
+            fn = lambda: api.fp4q_quantize(Xq, held, 448.0, api.ROW16, api.RNE, 0, 0, qc, qs, qS)  # noqa: E731
+        else:
+            if not prepared:
+                for k, f in ops:
+                    if not k.startswith("gemm"):
+                        f()  # the operands the measured launches read
+                prepared = True
+            fn = dict(ops)[name]
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(args.reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        print(json.dumps({"profile_op": name, "reps": args.reps,
+                          "us_per_call": round(a.elapsed_time(b) / args.reps * 1e3, 2)}), flush=True)
 
 
 def cpu_baseline(args, wl, M, N, K):

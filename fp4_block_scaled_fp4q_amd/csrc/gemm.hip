@@ -8,23 +8,26 @@
 // (v_mfma_f32_32x32x16_bf16) with fp32 accumulation.
 //
 // Design (gfx950):
-//  * A workgroup of 4 waves owns a 256 x 256 output tile; each wave a
-//    128 x 128 sub-tile (16 MFMA accumulators of 32 x 32).
+//  * A workgroup owns a 256 x 256 output tile; its 8 waves (2 along M x 4
+//    along N, two per SIMD) own 128 x 64 sub-tiles (8 MFMA accumulators of
+//    32 x 32 each).
 //  * K advances in tiles of 64. FP4 codes (0.5 B/element) and one scale byte
-//    per 16 elements are read from global memory one tile ahead into
-//    registers; every thread decodes one row of A and one row of B (64
-//    elements each) to bf16 and stores them in LDS, double buffered, while
-//    the MFMAs consume the other buffer. Decoding once per workgroup costs
-//    (256 + 256) * 64 elements per 256 * 256 * 64 MACs.
+//    per 16 elements are read from global memory two tiles ahead into
+//    registers; every thread decodes one 64-element row of the stacked
+//    [A tile; B tile] to bf16 into LDS, double buffered, in pieces placed
+//    between the MFMAs that consume the other buffer. Decoding once per
+//    workgroup costs (256 + 256) * 64 elements per 256 * 256 * 64 MACs.
 //  * Decode: v_cvt_scalef32_pk_f32_fp4 (scale 1.0) gives two exact E2M1
 //    values in fp32, one multiply each by the block's UE5M3 value (exact),
 //    and v_cvt_pk_bf16_f32 packs the exact products.
-//  * LDS rows are 8 chunks of 16 bytes (8 k each); chunk c of row r lives at
-//    slot c ^ (r & 7), so fragment reads (32 rows, one chunk) and the
-//    row-wise decode writes are both free of bank conflicts.
+//  * LDS rows are 8 chunks of 16 bytes (8 k each) at a 144-byte pitch, so
+//    any 16 consecutive rows fall on distinct banks for the fragment reads
+//    (32 rows, one chunk) and the row-wise decode writes.
 //  * Workgroups are numbered so that consecutive ones on one XCD (hardware
 //    dispatch is round-robin over the 8 XCDs) cover a compact group of tiles,
 //    which keeps their shared A and B rows in that XCD's L2.
+//  * Measured on the FFN shapes (16384 x 14336 x 4096 and its dgrad / wgrad)
+//    this runs at the rate of the vendor bf16 GEMM on plain bf16 operands.
 //
 // One kernel serves fwd (A = X, ROW16; B = W, TILE), dgrad (A = dY, ROW16;
 // B = W^T, TILE) and wgrad (A = dY^T, B = X^T, both quantized along tokens):
@@ -132,21 +135,33 @@ __device__ __forceinline__ uint32_t seg_word(const RowSeg& g, int c) {
   }
 }
 
-// Decode block j (chunks 2j, 2j+1) of a row segment into LDS row `row`.
-__device__ __forceinline__ void store_block(uint4* __restrict__ lds, const RowSeg& g, int row, int j) {
-  uint4* base = lds + row * kChunks;
-  const int sw = row & 7;
-  const float dec = ue5m3_value((g.s >> (8 * j)) & 0xFFu);
-  base[(2 * j) ^ sw] = decode8(seg_word(g, 2 * j), dec);
-  base[(2 * j + 1) ^ sw] = decode8(seg_word(g, 2 * j + 1), dec);
+// LDS slot of 16-byte chunk c of tile row r (8 chunks per 128-byte row).
+template <int kSwz>
+__device__ __forceinline__ int slot(int r, int c) {
+  if (kSwz == 2) return r * (kChunks + 1) + c;  // 144-byte row pitch
+  return r * kChunks + (kSwz == 0 ? (c ^ (r & 7)) : (c ^ ((r >> 1) & 7)));
 }
+template <int kSwz>
+constexpr int row_pitch() { return kSwz == 2 ? kChunks + 1 : kChunks; }
 
-template <bool kFullK, bool kF32Out>
-__global__ __launch_bounds__(kThreads) void gemm_kernel(
+// Workgroup = kWavesM x kWavesN waves over a 256 x 256 tile; wave tile
+// (256 / kWavesM) x (256 / kWavesN) built from 32 x 32 MFMA blocks.
+template <bool kFullK, bool kF32Out, int kWavesM, int kWavesN, int kSwz>
+__global__ __launch_bounds__(64 * kWavesM * kWavesN) void gemm_kernel(
     const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales, int a_shift,
     const float* __restrict__ a_S, const uint8_t* __restrict__ b_codes,
     const uint8_t* __restrict__ b_scales, int b_shift, const float* __restrict__ b_S, int64_t M,
     int64_t N, int64_t K, int tiles_m, int tiles_n, void* __restrict__ y) {
+  constexpr int kT = 64 * kWavesM * kWavesN;  // threads
+  constexpr int kTM = BM / kWavesM;           // wave tile rows
+  constexpr int kTN = BN / kWavesN;           // wave tile cols
+  constexpr int kFM = kTM / 32;               // MFMA blocks per wave along M
+  constexpr int kFN = kTN / 32;               // and along N
+  constexpr int kRows = (BM + BN) / kT;       // A/B tile rows each thread decodes
+  constexpr int kPieces = 2 * kRows;          // decode8 calls per thread per k16 step
+  constexpr int kMfmaPerPiece = kFM * kFN / kPieces;
+  static_assert(kFM * kFN % kPieces == 0, "MFMA count must split evenly");
+
   // 2 buffers x (A tile + B tile) = 128 KiB
   extern __shared__ uint4 lds[];
 
@@ -171,86 +186,92 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = wave >> 1;
-  const int wn = wave & 1;
+  const int wm = wave / kWavesN;
+  const int wn = wave % kWavesN;
   const int64_t m0 = (int64_t)tm * BM;
   const int64_t n0 = (int64_t)tn * BN;
 
-  f32x16 acc[4][4];
+  // rows this thread decodes: tile row q = tid + i * kT of the stacked
+  // [A tile; B tile] (A rows 0..255, B rows 256..511)
+  auto load_rows = [&](RowSeg* g, int64_t k0) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < kRows; ++i) {
+      const int q = tid + i * kT;
+      g[i] = q < BM ? load_seg<kFullK>(a_codes, a_scales, M, K, a_shift, m0 + q, k0)
+                    : load_seg<kFullK>(b_codes, b_scales, N, K, b_shift, n0 + (q - BM), k0);
+    }
+  };
+  // one decode8 piece p (0 .. kPieces-1) of block s into buffer `buf`
+  auto decode_piece = [&](uint4* buf, const RowSeg* g, int s, int p) {
+    const int i = p >> 1;
+    const int q = tid + i * kT;
+    const int c = 2 * s + (p & 1);
+    const float dec = ue5m3_value((g[i].s >> (8 * s)) & 0xFFu);
+    buf[slot<kSwz>(q, c)] = decode8(seg_word(g[i], c), dec);
+  };
+
+  f32x16 acc[kFM][kFN];
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+  for (int i = 0; i < kFM; ++i)
+#pragma unroll
+    for (int j = 0; j < kFN; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
   const int nk = (int)((K + BK - 1) / BK);
-  RowSeg ga, gb;  // codes of tile kt + 1, decoded during iteration kt
+  RowSeg g[kRows];  // codes of tile kt + 1, decoded during iteration kt
   if (nk > 0) {
-    ga = load_seg<kFullK>(a_codes, a_scales, M, K, a_shift, m0 + tid, 0);
-    gb = load_seg<kFullK>(b_codes, b_scales, N, K, b_shift, n0 + tid, 0);
+    load_rows(g, 0);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      store_block(lds, ga, tid, j);
-      store_block(lds + kTileChunks, gb, tid, j);
-    }
-    const int64_t k1 = (int64_t)min(1, nk - 1) * BK;
-    ga = load_seg<kFullK>(a_codes, a_scales, M, K, a_shift, m0 + tid, k1);
-    gb = load_seg<kFullK>(b_codes, b_scales, N, K, b_shift, n0 + tid, k1);
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int p = 0; p < kPieces; ++p) decode_piece(lds, g, s, p);
+    load_rows(g, (int64_t)min(1, nk - 1) * BK);
     __syncthreads();
   }
 
-  // lane's fragment rows inside the tile and their swizzle
-  const int arow0 = wm * 128 + (lane & 31);
-  const int brow0 = wn * 128 + (lane & 31);
+  const int arow0 = wm * kTM + (lane & 31);
+  const int brow0 = BM + wn * kTN + (lane & 31);
   const int hi = lane >> 5;
 
-  // fragment loads of one k16 step (A and B: 4 sub-tiles of 32 rows each)
-  auto load_frags = [&](const uint4* As, const uint4* Bs, int s, bf16x8* af, bf16x8* bfr) {
+  auto load_frags = [&](const uint4* buf, int s, bf16x8* af, bf16x8* bfr) {
     const int ch = 2 * s + hi;
 #pragma unroll
-    for (int t4 = 0; t4 < 4; ++t4) {
-      const int ar = arow0 + t4 * 32;
-      const int br = brow0 + t4 * 32;
-      af[t4] = __builtin_bit_cast(bf16x8, As[ar * kChunks + (ch ^ (ar & 7))]);
-      bfr[t4] = __builtin_bit_cast(bf16x8, Bs[br * kChunks + (ch ^ (br & 7))]);
-    }
+    for (int i = 0; i < kFM; ++i) af[i] = __builtin_bit_cast(bf16x8, buf[slot<kSwz>(arow0 + 32 * i, ch)]);
+#pragma unroll
+    for (int j = 0; j < kFN; ++j) bfr[j] = __builtin_bit_cast(bf16x8, buf[slot<kSwz>(brow0 + 32 * j, ch)]);
   };
 
   for (int kt = 0; kt < nk; ++kt) {
-    const uint4* As = lds + (kt & 1) * 2 * kTileChunks;
-    const uint4* Bs = As + kTileChunks;
-    uint4* An = lds + ((kt + 1) & 1) * 2 * kTileChunks;
+    constexpr int kBuf = (BM + BN) * row_pitch<kSwz>();
+    const uint4* cur_buf = lds + (kt & 1) * kBuf;
+    uint4* next_buf = lds + ((kt + 1) & 1) * kBuf;
     // codes of tile kt + 2 (the last tile again near the end: harmless)
-    const int64_t k2 = (int64_t)min(kt + 2, nk - 1) * BK;
-    const RowSeg na = load_seg<kFullK>(a_codes, a_scales, M, K, a_shift, m0 + tid, k2);
-    const RowSeg nb = load_seg<kFullK>(b_codes, b_scales, N, K, b_shift, n0 + tid, k2);
-    bf16x8 af[2][4], bfr[2][4];
-    load_frags(As, Bs, 0, af[0], bfr[0]);
+    RowSeg ng[kRows];
+    load_rows(ng, (int64_t)min(kt + 2, nk - 1) * BK);
+    bf16x8 af[2][kFM], bfr[2][kFN];
+    load_frags(cur_buf, 0, af[0], bfr[0]);
 #pragma unroll
     for (int s = 0; s < BK / 16; ++s) {
-      const int cur = s & 1;
-      if (s + 1 < BK / 16) load_frags(As, Bs, s + 1, af[cur ^ 1], bfr[cur ^ 1]);
-      // block s of the next tile (this thread's A row and B row) is decoded
-      // in four pieces, each after four MFMAs, so that the VALU work issues
-      // while the matrix core is busy
-      const float deca = ue5m3_value((ga.s >> (8 * s)) & 0xFFu);
-      const float decb = ue5m3_value((gb.s >> (8 * s)) & 0xFFu);
+      const int cb = s & 1;
+      if (s + 1 < BK / 16) load_frags(cur_buf, s + 1, af[cb ^ 1], bfr[cb ^ 1]);
+      // block s of the next tile is decoded in kPieces pieces, each after
+      // kMfmaPerPiece MFMAs, so that the VALU work issues while the matrix
+      // core is busy
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
+      for (int p = 0; p < kPieces; ++p) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[q][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][q], bfr[cur][j], acc[q][j], 0, 0, 0);
-        const bool is_a = q < 2;
-        const RowSeg& g = is_a ? ga : gb;
-        uint4* dst = (is_a ? An : An + kTileChunks) + tid * kChunks;
-        const int c = 2 * s + (q & 1);
-        dst[c ^ (tid & 7)] = decode8(seg_word(g, c), is_a ? deca : decb);
+        for (int u = 0; u < kMfmaPerPiece; ++u) {
+          const int f = p * kMfmaPerPiece + u;
+          const int i = f / kFN, j = f % kFN;
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cb][i], bfr[cb][j], acc[i][j], 0, 0, 0);
+        }
+        decode_piece(next_buf, g, s, p);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    ga = na;
-    gb = nb;
+#pragma unroll
+    for (int i = 0; i < kRows; ++i) g[i] = ng[i];
     __syncthreads();
   }
 
@@ -260,13 +281,13 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
   const bool alpha_normal = alpha >= 1.17549435e-38f && alpha <= 3.40282347e+38f;
   const bool full_tile = m0 + BM <= M && n0 + BN <= N;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < kFM; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t c = n0 + wn * 128 + j * 32 + (lane & 31);
+    for (int j = 0; j < kFN; ++j) {
+      const int64_t c = n0 + wn * kTN + j * 32 + (lane & 31);
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int64_t r = m0 + wm * 128 + i * 32 + 8 * (e >> 2) + 4 * hi + (e & 3);
+        const int64_t r = m0 + wm * kTM + i * 32 + 8 * (e >> 2) + 4 * hi + (e & 3);
         const float v = alpha_normal ? acc[i][j][e] * alpha : (float)((double)acc[i][j][e] * alpha_d);
         if (full_tile || (r < M && c < N)) {
           if (kF32Out) {
@@ -281,25 +302,42 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
 
 }  // namespace
 
+// Kernel configuration, chosen at build time: 2 x 4 waves (two per SIMD, so
+// one wave's MFMAs overlap the other's decode and LDS traffic; 128 x 64
+// accumulators each) and the padded 144-byte LDS row pitch, the fastest of
+// the measured variants (2x2 / 2x4 / 4x2 waves; XOR or padded layouts).
+#ifndef FP4Q_GEMM_WAVES_M
+#define FP4Q_GEMM_WAVES_M 2
+#endif
+#ifndef FP4Q_GEMM_WAVES_N
+#define FP4Q_GEMM_WAVES_N 4
+#endif
+#ifndef FP4Q_GEMM_SWZ
+#define FP4Q_GEMM_SWZ 2
+#endif
+
 hipError_t launch_gemm(const QOperand& a, const QOperand& b, void* y, int y_es, hipStream_t s) {
+  constexpr int WM = FP4Q_GEMM_WAVES_M, WN = FP4Q_GEMM_WAVES_N, SW = FP4Q_GEMM_SWZ;
   const int64_t M = a.rows, N = b.rows, K = a.cols;
   if (M == 0 || N == 0) return hipSuccess;
   const int tiles_m = (int)((M + BM - 1) / BM);
   const int tiles_n = (int)((N + BN - 1) / BN);
-  const size_t lds_bytes = 2 * 2 * kTileChunks * sizeof(uint4);
   const bool full_k = K % BK == 0;
+  const size_t lds_bytes = 2 * (BM + BN) * (SW == 2 ? kChunks + 1 : kChunks) * sizeof(uint4);
   const void* fn;
   if (full_k)
-    fn = y_es == 4 ? (const void*)gemm_kernel<true, true> : (const void*)gemm_kernel<true, false>;
+    fn = y_es == 4 ? (const void*)gemm_kernel<true, true, WM, WN, SW>
+                   : (const void*)gemm_kernel<true, false, WM, WN, SW>;
   else
-    fn = y_es == 4 ? (const void*)gemm_kernel<false, true> : (const void*)gemm_kernel<false, false>;
+    fn = y_es == 4 ? (const void*)gemm_kernel<false, true, WM, WN, SW>
+                   : (const void*)gemm_kernel<false, false, WM, WN, SW>;
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);
   if (e != hipSuccess) return e;
-  const dim3 grid((uint32_t)(tiles_m * tiles_n)), block(kThreads);
+  const dim3 grid((uint32_t)(tiles_m * tiles_n)), block(64 * WM * WN);
 #define FP4Q_GEMM(FK, F32)                                                                        \
-  hipLaunchKernelGGL((gemm_kernel<FK, F32>), grid, block, lds_bytes, s, a.codes, a.scales,        \
-                     a.tile ? 4 : 0, a.enc_scale, b.codes, b.scales, b.tile ? 4 : 0, b.enc_scale, \
-                     M, N, K, tiles_m, tiles_n, y)
+  hipLaunchKernelGGL((gemm_kernel<FK, F32, WM, WN, SW>), grid, block, lds_bytes, s, a.codes,      \
+                     a.scales, a.tile ? 4 : 0, a.enc_scale, b.codes, b.scales, b.tile ? 4 : 0,    \
+                     b.enc_scale, M, N, K, tiles_m, tiles_n, y)
   if (full_k) {
     if (y_es == 4) FP4Q_GEMM(true, true);
     else FP4Q_GEMM(true, false);

@@ -5,11 +5,10 @@ One step = the whole hot path on the FFN up-projection shape
 (X 16384x4096 bf16, W 14336x4096 bf16, dY 16384x14336 bf16), as a refresh
 step of sample-and-hold tensor scaling:
   amax(X), amax(W), amax(dY)
-  quantize X  ROW16 RNE          (fwd operand)
+  quantize X  ROW16 + COL16 RNE (fwd operand; wgrad operand along tokens), one pass
   quantize W  TILE16x16 RNE + transposed copy (fwd and dgrad operand)
-  quantize dY ROW16 SR           (dgrad operand)
-  quantize dY COL16 SR           (wgrad operand, along tokens)
-  quantize X  COL16 RNE          (wgrad operand, along tokens)
+  quantize dY ROW16 + COL16 SR  (dgrad operand; wgrad operand along tokens), one
+              pass, one Philox word per element for both
   Y  = Xq Wq^T     (bf16 out)    fwd
   dX = dYq Wq      (bf16 out)    dgrad
   dW = dYq^T Xq    (fp32 out)    wgrad
@@ -83,16 +82,16 @@ def main():
     u8 = dict(dtype=torch.uint8, device=dev)
     f32 = dict(dtype=torch.float32, device=dev)
     amax = {k: torch.empty(1, **f32) for k in ("X", "W", "dY")}
-    S = {k: torch.empty(1, **f32) for k in ("x", "w", "dy", "dyt", "xt")}
+    S = {k: torch.empty(1, **f32) for k in ("x", "w", "dy")}
     xq = api.QTensor(torch.empty((M, K // 2), **u8), torch.empty((M, K // 16), **u8), S["x"], M, K, api.ROW16)
     wq = api.QTensor(torch.empty((N, K // 2), **u8), torch.empty((N // 16, K // 16), **u8), S["w"], N, K,
                      api.TILE16x16)
     wqt = api.QTensor(torch.empty((K, N // 2), **u8), torch.empty((K // 16, N // 16), **u8), S["w"], K, N,
                       api.TILE16x16)
     dyq = api.QTensor(torch.empty((M, N // 2), **u8), torch.empty((M, N // 16), **u8), S["dy"], M, N, api.ROW16)
-    dyqt = api.QTensor(torch.empty((N, M // 2), **u8), torch.empty((N, M // 16), **u8), S["dyt"], N, M,
+    dyqt = api.QTensor(torch.empty((N, M // 2), **u8), torch.empty((N, M // 16), **u8), S["dy"], N, M,
                        api.ROW16)
-    xqt = api.QTensor(torch.empty((K, M // 2), **u8), torch.empty((K, M // 16), **u8), S["xt"], K, M, api.ROW16)
+    xqt = api.QTensor(torch.empty((K, M // 2), **u8), torch.empty((K, M // 16), **u8), S["x"], K, M, api.ROW16)
     Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     dX = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
     dW = torch.empty((N, K), **f32)
@@ -104,16 +103,15 @@ def main():
         ("amax", lambda: api.fp4q_amax(X, amax["X"])),
         ("amax", lambda: api.fp4q_amax(W, amax["W"])),
         ("amax", lambda: api.fp4q_amax(dY, amax["dY"])),
-        ("quant_x_row16", lambda: api.fp4q_quantize(X, amax["X"], T, api.ROW16, api.RNE, 0, 0,
-                                                    xq.codes, xq.scales, S["x"])),
+        # X: ROW16 (fwd) and COL16 (wgrad) in one pass
+        ("quant_x_row_col", lambda: api.fp4q_quantize(X, amax["X"], T, api.ROW16, api.RNE, 0, 0,
+                                                      xq.codes, xq.scales, S["x"], xqt.codes, xqt.scales)),
         ("quant_w_tile", lambda: api.fp4q_quantize(W, amax["W"], T, api.TILE16x16, api.RNE, 0, 0,
                                                    wq.codes, wq.scales, S["w"], wqt.codes, wqt.scales)),
-        ("quant_dy_row16_sr", lambda: api.fp4q_quantize(dY, amax["dY"], T, api.ROW16, api.SR, seed, 0,
-                                                        dyq.codes, dyq.scales, S["dy"])),
-        ("quant_dy_col16_sr", lambda: api.fp4q_quantize(dY, amax["dY"], T, api.COL16, api.SR, seed, 0,
-                                                        dyqt.codes, dyqt.scales, S["dyt"])),
-        ("quant_x_col16", lambda: api.fp4q_quantize(X, amax["X"], T, api.COL16, api.RNE, 0, 0,
-                                                    xqt.codes, xqt.scales, S["xt"])),
+        # dY: ROW16 (dgrad) and COL16 (wgrad) in one pass, one Philox word per element
+        ("quant_dy_row_col_sr", lambda: api.fp4q_quantize(dY, amax["dY"], T, api.ROW16, api.SR, seed, 0,
+                                                          dyq.codes, dyq.scales, S["dy"], dyqt.codes,
+                                                          dyqt.scales)),
         ("gemm_fwd", lambda: api.fp4q_linear_fwd(xq, wq, Y)),
         ("gemm_dgrad", lambda: api.fp4q_linear_dgrad(dyq, wqt, dX)),
         ("gemm_wgrad", lambda: api.fp4q_linear_wgrad(dyqt, xqt, dW)),
@@ -169,9 +167,9 @@ def main():
         return b
     codec_bytes = {
         "amax": (M * K + N * K + M * N) * 2 / 3.0,  # average of the three launches
-        "quant_x_row16": qbytes(M, K, 2), "quant_w_tile": qbytes(N, K, 2, True) - N * K / 16 + N * K / 256,
-        "quant_dy_row16_sr": qbytes(M, N, 2), "quant_dy_col16_sr": qbytes(M, N, 2),
-        "quant_x_col16": qbytes(M, K, 2),
+        "quant_x_row_col": qbytes(M, K, 2) + M * K * (0.5 + 1 / 16),
+        "quant_w_tile": qbytes(N, K, 2, True) - N * K / 16 + N * K / 256,
+        "quant_dy_row_col_sr": qbytes(M, N, 2) + M * N * (0.5 + 1 / 16),
     }
     codec_gbs = {k: codec_bytes[k] / (kern[k] * 1e-6) / 1e9 for k in codec_bytes}
 

@@ -129,8 +129,10 @@ def quantize(x: torch.Tensor, amax_held: torch.Tensor, target: float = 448.0, la
     """Allocate outputs and run fp4q_quantize.
 
     Returns (q, qt, diag): q is the operand as the GEMMs read it (for COL16,
-    the [cols, rows] transpose stored ROW16), qt the transposed TILE copy or
-    None, diag the int32[2] repair counts or None.
+    the [cols, rows] transpose stored ROW16); with transposed=True, qt is the
+    other orientation (TILE: the transposed tile copy; ROW16: the COL16
+    operand [cols, rows] of the same tensor), else None; diag the int32[2]
+    repair counts or None.
     """
     _dev2d(x, "x")
     R, C = x.shape
@@ -146,7 +148,7 @@ def quantize(x: torch.Tensor, amax_held: torch.Tensor, target: float = 448.0, la
     codes_t = scales_t = None
     if transposed:
         codes_t = torch.empty((C, R // 2), **u8)
-        scales_t = torch.empty((C // 16, R // 16), **u8)
+        scales_t = torch.empty((C // 16, R // 16) if layout == TILE16x16 else (C, R // 16), **u8)
     diag = torch.empty(2, dtype=torch.int32, device=dev) if with_diag else None
     fp4q_quantize(x, amax_held, target, layout, rnd, seed, subseq, codes, scales, S,
                   codes_t, scales_t, diag)
@@ -154,7 +156,7 @@ def quantize(x: torch.Tensor, amax_held: torch.Tensor, target: float = 448.0, la
         q = QTensor(codes, scales, S, C, R, ROW16)
     else:
         q = QTensor(codes, scales, S, R, C, layout)
-    qt = QTensor(codes_t, scales_t, S, C, R, TILE16x16) if transposed else None
+    qt = QTensor(codes_t, scales_t, S, C, R, layout) if transposed else None
     return q, qt, diag
 
 

@@ -4,9 +4,9 @@
 // HBM-bound: every byte is read once with 128-bit loads. The maximum is taken
 // over sign-cleared bit patterns, which order like the magnitudes of finite
 // values, so the result is exact and independent of the reduction order.
-// bf16 pairs are reduced with packed 16-bit integer max; each wave reduces
-// across lanes and issues one 32-bit atomic max on the output word (non-
-// negative floats order like their bit patterns).
+// bf16 pairs are reduced with packed 16-bit integer max; each workgroup
+// reduces across its lanes and issues at most one 32-bit atomic max on the
+// output word (non-negative floats order like their bit patterns).
 #include "codec.h"
 #include "kernels.h"
 
@@ -31,12 +31,21 @@ __device__ __forceinline__ uint32_t fold(uint32_t acc, const uint4 v) {
   return max(acc, max(max(w0, w1), max(w2, w3)));
 }
 
+// Workgroup-wide maximum, then at most one atomic per workgroup, skipped
+// when the output already holds a value at least as large (atomics on one
+// address serialize, so their number is kept to a few hundred).
 template <bool kBF16>
 __device__ __forceinline__ void finish(uint32_t acc, uint32_t* out) {
+  __shared__ uint32_t wmax[4];
   uint32_t m = kBF16 ? (max(acc & 0xFFFFu, acc >> 16) << 16) : acc;
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
-  if ((threadIdx.x & 63) == 0 && m != 0u) atomicMax(out, m);
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    m = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
+    if (m > __hip_atomic_load(out, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) atomicMax(out, m);
+  }
 }
 
 // Contiguous tensor (ld == cols): a flat grid-stride walk over 16-byte
@@ -86,7 +95,7 @@ hipError_t launch_amax(const void* x, int es, int64_t rows, int64_t cols, int64_
   if (ld == cols) {
     const int64_t nchunks = rows * chunks_per_row;
     int64_t wgs = (nchunks + 4 * 256 - 1) / (4 * 256);
-    if (wgs > 4096) wgs = 4096;
+    if (wgs > 1024) wgs = 1024;
     if (es == 2)
       hipLaunchKernelGGL(amax_flat_kernel<true>, dim3((uint32_t)wgs), dim3(256), 0, s,
                          (const uint4*)x, nchunks, o);
@@ -95,7 +104,7 @@ hipError_t launch_amax(const void* x, int es, int64_t rows, int64_t cols, int64_
                          (const uint4*)x, nchunks, o);
     return hipGetLastError();
   }
-  const int64_t target_wgs = 4096;
+  const int64_t target_wgs = 1024;
   int64_t rows_per_wg = (rows + target_wgs - 1) / target_wgs;
   const int64_t wgs = (rows + rows_per_wg - 1) / rows_per_wg;
   if (es == 2)

@@ -12,7 +12,6 @@
 namespace {
 
 constexpr int64_t kMaxGridX = 0x7FFFFFFF / 256;  // workgroups of 256 threads
-constexpr int64_t kMaxGridY = 65535;
 
 int elem_size(int dt) { return dt == FP4Q_F32 ? 4 : (dt == FP4Q_BF16 ? 2 : 0); }
 
@@ -28,7 +27,7 @@ fp4q_status check_operand(const fp4q_qtensor* q) {
   if (q->layout == FP4Q_TILE16x16 && q->rows % 16) return FP4Q_E_SHAPE;
   if (!q->enc_scale) return FP4Q_E_NULL;
   if (q->rows > 0 && q->cols > 0 && (!q->codes || !q->scales)) return FP4Q_E_NULL;
-  if (!aligned(q->codes, 8)) return FP4Q_E_ALIGN;
+  if (!aligned(q->codes, 8) || !aligned(q->scales, 4)) return FP4Q_E_ALIGN;
   return FP4Q_OK;
 }
 
@@ -53,7 +52,7 @@ fp4q_status gemm(const fp4q_qtensor* a, const fp4q_qtensor* b, void* y, fp4q_dty
   if (!es) return FP4Q_E_DTYPE;
   if (a->cols != b->cols) return FP4Q_E_SHAPE;
   if (a->rows > 0 && b->rows > 0 && !y) return FP4Q_E_NULL;
-  if ((b->rows + 127) / 128 > kMaxGridX || (a->rows + 127) / 128 > kMaxGridY) return FP4Q_E_SHAPE;
+  if (((a->rows + 255) / 256) * ((b->rows + 255) / 256) > 0x7FFFFFFF / 512) return FP4Q_E_SHAPE;
   return from_hip(fp4q::launch_gemm(to_operand(a), to_operand(b), y, es,
                                     static_cast<hipStream_t>(stream)));
 }
@@ -103,7 +102,9 @@ fp4q_status fp4q_quantize(const void* x, fp4q_dtype xt, int64_t rows, int64_t co
   if (rnd != FP4Q_RNE && rnd != FP4Q_SR) return FP4Q_E_ARG;
   if (!(target > 0.0f) || !std::isfinite(target)) return FP4Q_E_ARG;
   if ((codes_t == nullptr) != (scales_t == nullptr)) return FP4Q_E_ARG;
-  if (codes_t && layout != FP4Q_TILE16x16) return FP4Q_E_ARG;
+  if (codes_t && layout == FP4Q_COL16) return FP4Q_E_ARG;
+  // ROW16 with the second orientation also needs whole column blocks
+  if (codes_t && layout == FP4Q_ROW16 && rows % 16) return FP4Q_E_SHAPE;
   if (!amax_held) return FP4Q_E_NULL;
   if (rows < 0 || cols < 0 || ld < cols) return FP4Q_E_SHAPE;
   if (layout != FP4Q_COL16 && cols % 16) return FP4Q_E_SHAPE;
@@ -114,12 +115,11 @@ fp4q_status fp4q_quantize(const void* x, fp4q_dtype xt, int64_t rows, int64_t co
     if (!x || !codes || !scales) return FP4Q_E_NULL;
     if (!aligned(x, 16) || (ld * es) % 16) return FP4Q_E_ALIGN;
     if (!aligned(codes, 8) || (codes_t && !aligned(codes_t, 8))) return FP4Q_E_ALIGN;
-    if (layout == FP4Q_ROW16) {
-      const int64_t chunks = cols / 8;
-      const int64_t segs = (chunks + 255) / 256;
+    if (layout == FP4Q_ROW16 && !codes_t) {
+      const int64_t segs = (cols / 16 + 255) / 256;
       if (rows * segs > kMaxGridX) return FP4Q_E_SHAPE;
-    } else {
-      if ((cols / 8 + 255) / 256 > kMaxGridX || rows / 16 > kMaxGridY) return FP4Q_E_SHAPE;
+    } else if (((cols / 8 + 255) / 256) * ((rows / 16 + 3) / 4) > kMaxGridX) {
+      return FP4Q_E_SHAPE;
     }
   }
   if ((enc_scale_out && !aligned(enc_scale_out, 4)) || (diag && !aligned(diag, 4)))

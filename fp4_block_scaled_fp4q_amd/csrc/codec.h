@@ -53,120 +53,96 @@ __device__ __forceinline__ uint4 load_nt16(const void* p) {
 // a code that rounds to 0 becomes 0x01, one that rounds beyond 61,440
 // (raw >= 63,488, the midpoint to 2^16, tie to the even side) becomes 0xF7.
 // flags: bit 0 zero-rounded, bit 1 saturated (both before repair).
+//  * raw >= 2^-14 (normal UE5M3): the code is the binary32 pattern rounded
+//    to 3 fraction bits (RNE by adding 0x7FFFF plus the kept lsb, a carry
+//    moving into the exponent), shifted down and rebased from bias 127 to 15.
+//  * raw < 2^-14 (subnormal UE5M3, code = RN(raw * 2^17) in 0..8): the
+//    exact product raw * 2^17 < 8 is rounded to an integer by adding 2^23.
 __device__ __forceinline__ uint32_t ue5m3_encode(float raw, uint32_t* flags) {
   const uint32_t u = f2u(raw);
-  if (u >= 0x47780000u) {  // raw >= 63488.0f, or +Inf
-    *flags = 2u;
-    return 0xF7u;
-  }
-  const uint32_t e32 = u >> 23;
-  uint32_t code;
-  if (e32 >= 113u) {
-    // normal range of UE5M3 (>= 2^-14): keep 3 fraction bits, RNE on 20
-    const uint32_t m = u & 0x7FFFFFu;
-    const uint32_t base = ((e32 - 112u) << 3) | (m >> 20);
-    const uint32_t rem = m & 0xFFFFFu;
-    const uint32_t up = (rem > 0x80000u) | ((rem == 0x80000u) & (base & 1u));
-    code = base + up;  // a carry moves into the exponent field
-  } else if (e32 == 0u) {
-    code = 0u;  // +0 or an fp32 denormal (< 2^-126)
-  } else {
-    // subnormal range: code = RN(raw * 2^17), value = code * 2^-17
-    const uint32_t sig = (u & 0x7FFFFFu) | 0x800000u;
-    const uint32_t sh = 133u - e32;  // >= 21
-    if (sh >= 25u) {
-      code = 0u;  // raw < 2^-18, strictly below the half-way point
-    } else {
-      const uint32_t base = sig >> sh;
-      const uint32_t rem = sig & ((1u << sh) - 1u);
-      const uint32_t half = 1u << (sh - 1u);
-      const uint32_t up = (rem > half) | ((rem == half) & (base & 1u));
-      code = base + up;
-    }
-  }
-  if (code == 0u) {
-    *flags = 1u;
-    return 1u;
-  }
-  *flags = 0u;
-  return code;
+  const uint32_t normal = ((u + 0x7FFFFu + ((u >> 20) & 1u)) >> 20) - (112u << 3);
+  const uint32_t sub = f2u(raw * 131072.0f + 8388608.0f) - 0x4B000000u;
+  uint32_t code = u >= 0x38800000u ? normal : sub;  // 2^-14
+  const bool sat = u >= 0x47780000u;                 // raw >= 63488 (or +Inf)
+  const bool zero = code == 0u;
+  *flags = (zero ? 1u : 0u) | (sat ? 2u : 0u);
+  code = zero ? 1u : code;
+  return sat ? 0xF7u : code;
+}
+
+// RN(a / 6) for finite a >= 0, computed as RN32(RN64(a * RN64(1/6))). This
+// equals the correctly rounded binary32 quotient: the exact quotient of a
+// 24-bit significand by 3 stays at least 2^-26 (relative) away from every
+// binary32 rounding midpoint, far more than the < 2^-52 error of the double
+// product.
+__device__ __forceinline__ float div6_rn(float a) { return (float)((double)a * (1.0 / 6.0)); }
+
+// RN(s / d) for s > 0 and d a positive UE5M3 value, as RN32(s * 1/d) in
+// double with a Newton-refined reciprocal. d = (8 + m) 2^k with an odd part
+// of 8 + m in {1, 3, 5, ..., 15}: the quotient is either exact or at least
+// 2^-29 (relative) away from every binary32 midpoint, again far more than
+// the double error.
+__device__ __forceinline__ float div_rn(double s, float d) {
+  const double dd = (double)d;
+  double y = __builtin_amdgcn_rcp(dd);
+  y = __builtin_fma(y, __builtin_fma(-dd, y, 1.0), y);
+  return (float)(s * y);
 }
 
 // Per-block quantities shared by every element of a block.
 struct BlockScale {
-  uint32_t code;   // UE5M3 code written to the scale array
-  float mul;       // r = RN(S / dec); multiplies each element
-  uint32_t flags;  // repair flags
-  bool zero;       // bamax == 0: scale 0, sign-only payloads
-  bool mul_inf;    // r overflowed: payload is 6 for x != 0, 0 for x == 0
+  uint32_t code;  // UE5M3 code written to the scale array (0 for an all-zero block)
+  float mul;      // r = RN(S / dec); 0 for an all-zero block, so x * r keeps only the sign
+  uint32_t flags; // repair flags
 };
 
-__device__ __forceinline__ BlockScale block_scale(float bamax, float S) {
-  BlockScale b;
-  if (!(bamax > 0.0f)) {
-    b.code = 0u;
-    b.mul = 0.0f;
-    b.flags = 0u;
-    b.zero = true;
-    b.mul_inf = false;
-    return b;
-  }
-  const float d6 = bamax / 6.0f;
+// bamax is the block's max |x| as a sign-cleared bit pattern.
+__device__ __forceinline__ BlockScale block_scale(uint32_t bamax, float S, double S_d) {
+  const float d6 = div6_rn(u2f(bamax));
   const float raw = d6 * S;
-  b.code = ue5m3_encode(raw, &b.flags);
-  const float dec = ue5m3_value(b.code);
-  b.mul = S / dec;
-  b.zero = false;
-  b.mul_inf = __builtin_isinf(b.mul);
+  uint32_t flags;
+  const uint32_t code = ue5m3_encode(raw, &flags);
+  const float mul = div_rn(S_d, ue5m3_value(code));
+  BlockScale b;
+  const bool nz = bamax != 0u;
+  b.code = nz ? code : 0u;
+  b.flags = nz ? flags : 0u;
+  b.mul = nz ? mul : 0.0f;
   return b;
 }
 
-// E2M1 magnitude code (0..7) of |v| by round to nearest, ties to the even
-// code, saturating at 6 (code 7). The magic-constant addition rounds |v| to
-// the E2M1 spacing of its binade (0.5 below 2, 1 in [2, 4), 2 from 4) with
-// the hardware's own RNE; the low bits of the sum are then the code offset
-// inside that binade. |v| is clamped to 8 first so that huge values and Inf
-// stay in range (8 rounds to code 8, clamped to 7). NaN cannot reach here.
-__device__ __forceinline__ uint32_t e2m1_rne_mag(float v) {
-  const float a = __builtin_fminf(__builtin_fabsf(v), 8.0f);
-  const bool ge2 = a >= 2.0f;
-  const bool ge4 = a >= 4.0f;
-  const float magic = ge4 ? 16777216.0f : (ge2 ? 8388608.0f : 4194304.0f);
-  const uint32_t off = ge4 ? 4u : (ge2 ? 2u : 0u);
-  const float t = a + magic;
-  const uint32_t q = (f2u(t) & 0xFu) + off;
-  return q < 7u ? q : 7u;
+// RNE payload codes of two values packed in byte `sel` of `word`: the gfx950
+// conversion v_cvt_scalef32_pk_fp4_f32 with scale 1.0 rounds to nearest,
+// ties to the even code, saturates at 6 and keeps the sign of zero; this was
+// checked against the reference rule for every bf16 input and is covered by
+// the parity tests for fp32 inputs.
+#define FP4Q_ENC2(word, a, b, sel) __builtin_amdgcn_cvt_scalef32_pk_fp4_f32((word), (a), (b), 1.0f, (sel))
+
+// Stochastic rounding of v to an E2M1 code (sign | magnitude) with the
+// 32-bit word w: rounds |v| up to the next magnitude iff w < ceil(p 2^32),
+// p the position of |v| between its two neighbours (w < ceil(x) is w < x for
+// an integer w). In units of 0.5 the grid is 0, 1, 2, 3, 4 then 4, 6, 8 and
+// 8, 12: with A = 2|v|, e = clamp(exponent(A) - 2, 0, 2) and B = A / 2^e,
+// the lower neighbour has code 2e + floor(B) and p = frac(B), both exact in
+// binary32, so p 2^32 is exact before the ceiling. A is clamped to 12, so
+// |v| >= 6 (and Inf) lands exactly on code 7 with p = 0.
+__device__ __forceinline__ uint32_t sr_code(float v, uint32_t w) {
+  const uint32_t u = f2u(v);
+  const float a2 = __builtin_fminf(u2f(u & 0x7FFFFFFFu) * 2.0f, 12.0f);
+  const uint32_t ea = f2u(a2) >> 23;
+  const uint32_t e = min(max(ea, 128u), 130u) - 128u;
+  const float b = __builtin_ldexpf(a2, -(int)e);
+  const float fl = __builtin_floorf(b);
+  const uint32_t t = (uint32_t)__builtin_ceilf((b - fl) * 4294967296.0f);
+  const uint32_t mag = 2u * e + (uint32_t)fl + (w < t ? 1u : 0u);
+  return ((u >> 28) & 8u) | mag;
 }
 
-// Stochastic rounding between the adjacent E2M1 magnitudes lo <= |v| < hi:
-// rounds up iff w < ceil(p * 2^32) with p = (|v| - lo) / (hi - lo), computed
-// in binary32 (exact: Sterbenz for the difference, a power-of-two gap).
-// |v| >= 6 gives 6. NaN cannot reach here.
-__device__ __forceinline__ uint32_t e2m1_sr_mag(float v, uint32_t w) {
-  const float a = __builtin_fabsf(v);
-  if (a >= 6.0f) return 7u;
-  // lower neighbour index q and its value / gap
-  uint32_t q;
-  float lo, inv_gap;
-  if (a < 2.0f) {
-    q = (uint32_t)(a * 2.0f);  // floor: exact for a < 2
-    lo = (float)q * 0.5f;
-    inv_gap = 2.0f;
-  } else if (a < 4.0f) {
-    const uint32_t k = (uint32_t)a;  // 2 or 3
-    q = k + 2u;
-    lo = (float)k;
-    inv_gap = 1.0f;
-  } else {
-    q = 6u;
-    lo = 4.0f;
-    inv_gap = 0.5f;
-  }
-  const float p = (a - lo) * inv_gap;  // exact
-  const float thr = __builtin_ceilf(p * 4294967296.0f);
-  // thr <= 2^32 - 256 fits in uint32 after the cast for p < 1
-  const uint32_t t = (uint32_t)thr;
-  return q + (w < t ? 1u : 0u);
+// Payload code when r overflowed (possible only for a tiny held amax):
+// x * r is +-Inf (code 6) for x != 0 and 0 * Inf for x == 0, encoded as a
+// signed zero.
+__device__ __forceinline__ uint32_t inf_code(float x) {
+  return ((f2u(x) >> 28) & 8u) | (x != 0.0f ? 7u : 0u);
 }
 
 // ---------------------------------------------------------------- Philox
@@ -205,17 +181,6 @@ __device__ __forceinline__ U4 sr_words(uint64_t j, uint32_t subseq, uint64_t see
   c.z = subseq;
   c.w = 0u;
   return philox4x32_10(c, (uint32_t)seed, (uint32_t)(seed >> 32));
-}
-
-// Payload code (sign | magnitude) for one element, RNE or SR.
-template <bool kSR>
-__device__ __forceinline__ uint32_t payload_code(float x, const BlockScale& b, uint32_t w) {
-  const uint32_t sign = (f2u(x) >> 28) & 8u;
-  if (b.zero) return sign;
-  if (b.mul_inf) return sign | (x != 0.0f ? 7u : 0u);
-  const float v = x * b.mul;
-  const uint32_t mag = kSR ? e2m1_sr_mag(v, w) : e2m1_rne_mag(v);
-  return sign | mag;
 }
 
 // bf16 -> fp32 widening of a packed pair.

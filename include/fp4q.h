@@ -66,7 +66,7 @@ typedef enum {
  * (scales [rows][cols/16]; also what FP4Q_COL16 produces for the transpose)
  * or FP4Q_TILE16x16 (scales [rows/16][cols/16]). enc_scale points to the
  * device fp32 tensor scale S written by fp4q_quantize. codes must be 8-byte
- * aligned. */
+ * aligned and scales 4-byte aligned. */
 typedef struct {
     const uint8_t *codes;
     const uint8_t *scales;
@@ -111,8 +111,13 @@ fp4q_status fp4q_amax(const void *x, fp4q_dtype xt, int64_t rows, int64_t cols, 
  *  layout: FP4Q_ROW16 needs cols % 16 == 0; FP4Q_COL16 rows % 16 == 0 and
  *    cols % 8 == 0; FP4Q_TILE16x16 rows % 16 == 0 and cols % 16 == 0.
  *  codes / scales: outputs in the layout's shape (see fp4q_layout).
- *  codes_t / scales_t: FP4Q_TILE16x16 only, both or neither: the transposed
- *    copy (codes [cols][rows/2], scales [cols/16][rows/16]) that dgrad reads.
+ *  codes_t / scales_t: both or neither; not with FP4Q_COL16.
+ *    FP4Q_TILE16x16: the transposed copy (codes [cols][rows/2], scales
+ *      [cols/16][rows/16]) that dgrad reads.
+ *    FP4Q_ROW16: the COL16 quantization of the same tensor (codes
+ *      [cols][rows/2], scales [cols][rows/16]; needs rows % 16 == 0),
+ *      produced in the same pass: one read of x and, for SR, one Philox word
+ *      per element serving both orientations (fwd/dgrad and wgrad operands).
  *  diag (device, optional, two int32): receives the number of blocks whose
  *    scale was zero-rounded and saturated before repair.
  *  Alignment: x 16-byte aligned, ld * sizeof(elem) a multiple of 16; codes

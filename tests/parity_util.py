@@ -46,6 +46,11 @@ def quant_both(x: torch.Tensor, amax_held: float, layout: str, rnd: int = 0, T: 
         g["codes_t"] = qt.codes.cpu().numpy()
         g["scales_t"] = qt.scales.cpu().numpy()
     o = oracle.quantize(host_view(x), amax_held, T, lay_o, rnd, seed, subseq, transposed=transposed)
+    if layout == "row16" and transposed:
+        # the second orientation of a ROW16 call is the COL16 quantization
+        oc = oracle.quantize(host_view(x), amax_held, T, oracle.COL16, rnd, seed, subseq)
+        o.qt = oc.q
+        o.diag = o.diag + oc.diag
     return g, o
 
 

@@ -56,7 +56,8 @@ def test_quantize_validation():
     assert quant(target=float("inf")) == _lib.E_ARG
     assert quant(target=float("nan")) == _lib.E_ARG
     assert quant(ct=FAKE) == _lib.E_ARG                       # codes_t without scales_t
-    assert quant(ct=FAKE, st=FAKE) == _lib.E_ARG              # transposed copy needs TILE
+    assert quant(ct=FAKE, st=FAKE, layout=_lib.COL16) == _lib.E_ARG  # no second orientation for COL16
+    assert quant(ct=FAKE, st=FAKE, rows=24) == _lib.E_SHAPE   # ROW16 + COL16 needs rows % 16
     assert quant(amax=None) == _lib.E_NULL
     assert quant(x=None) == _lib.E_NULL
     assert quant(codes=None) == _lib.E_NULL
@@ -95,6 +96,8 @@ def test_gemm_and_dequant_validation():
         assert fn(a, b, None, _lib.BF16, None) == _lib.E_NULL
         assert fn(q(32, 64, S=None), b, FAKE, _lib.BF16, None) == _lib.E_NULL
         assert fn(q(32, 64, codes=FAKE_ODD), b, FAKE, _lib.BF16, None) == _lib.E_ALIGN
+        assert fn(a, q(48, 64, _lib.TILE16x16, scales=ctypes.c_void_p(0x10002)), FAKE, _lib.BF16,
+                  None) == _lib.E_ALIGN
     assert L.fp4q_dequant(q(32, 64), None, _lib.F32, None) == _lib.E_NULL
     assert L.fp4q_dequant(q(32, 64), FAKE_ODD, _lib.F32, None) == _lib.E_ALIGN
     assert L.fp4q_dequant(q(32, 64), FAKE, 9, None) == _lib.E_DTYPE

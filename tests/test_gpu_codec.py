@@ -43,7 +43,8 @@ def test_amax(dtype, shape, pad):
 
 
 CASES = [("row16", (37, 4128)), ("row16", (16, 64)), ("col16", (48, 1048)), ("col16", (32, 4104)),
-         ("tile", (48, 1056)), ("tile", (64, 4128))]
+         ("col16", (208, 4104)), ("tile", (48, 1056)), ("tile", (64, 4128)), ("tile", (208, 528)),
+         ("row16+col16", (48, 1056)), ("row16+col16", (208, 4128))]
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
@@ -52,9 +53,11 @@ CASES = [("row16", (37, 4128)), ("row16", (16, 64)), ("col16", (48, 1048)), ("co
 def test_quantize_parity(layout, shape, rnd, dtype):
     x = _grad(shape, 3, dtype) if rnd else _t3(shape, 2, dtype)
     a = float(oracle.amax(host_view(x)))
+    both = layout == "row16+col16"
+    lay = "row16" if both else layout
     for held, T in ((a, 448.0), (a * 0.01, 448.0), (a * 300.0, 2048.0)):
-        g, o = quant_both(x, held, layout, rnd, T, seed=0x5EED_0001_0000_0007, subseq=2,
-                          transposed=(layout == "tile"))
+        g, o = quant_both(x, held, lay, rnd, T, seed=0x5EED_0001_0000_0007, subseq=2,
+                          transposed=(layout == "tile" or both))
         assert_quant_equal(g, o, f"{layout} {shape} rnd={rnd} held={held} T={T}")
 
 
@@ -65,6 +68,8 @@ def test_quantize_strided_rows():
     g, o = quant_both(x, 3.0, "col16", ld_pad=8)
     assert_quant_equal(g, o)
     g, o = quant_both(x, 3.0, "tile", transposed=True, ld_pad=16)
+    assert_quant_equal(g, o)
+    g, o = quant_both(x, 3.0, "row16", transposed=True, ld_pad=24)
     assert_quant_equal(g, o)
 
 
@@ -131,10 +136,10 @@ def test_degenerate_tensor_scales(held):
     x = _t3((32, 64), 5, torch.float32)
     x[3] = 0.0                          # all-zero blocks
     x[4, :16] = 1e-30
-    for layout in ("row16", "col16", "tile"):
+    for layout, tr in (("row16", False), ("row16", True), ("col16", False), ("tile", True)):
         for rnd in (0, 1):
-            g, o = quant_both(x, held, layout, rnd, transposed=(layout == "tile"))
-            assert_quant_equal(g, o, f"held={held} {layout} rnd={rnd}")
+            g, o = quant_both(x, held, layout, rnd, transposed=tr)
+            assert_quant_equal(g, o, f"held={held} {layout} tr={tr} rnd={rnd}")
 
 
 def test_empty_quantize_writes_scale():

@@ -74,11 +74,13 @@ def test_linear_small_fwd_dgrad_wgrad():
     ax, aw, ady = (float(oracle.amax(host_view(t))) for t in (X, W, dY))
     gx, ox = quant_both(X, ax, "row16")
     gw, ow = quant_both(W, aw, "tile", transposed=True)
-    gdy, ody = quant_both(dY, ady, "row16", rnd=1, seed=5)
+    gdy, ody = quant_both(dY, ady, "row16", rnd=1, seed=5, transposed=True)  # + COL16 in one pass
     gdyt, odyt = quant_both(dY, ady, "col16", rnd=1, seed=5)
     gxt, oxt = quant_both(X, ax, "col16")
     for g, o in ((gx, ox), (gw, ow), (gdy, ody), (gdyt, odyt), (gxt, oxt)):
         assert_quant_equal(g, o)
+    # the dual pass's COL16 output equals the COL16-only call
+    np.testing.assert_array_equal(gdy["codes_t"], gdyt["codes"])
     y = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
     dx = torch.empty((M, K), dtype=torch.bfloat16, device=DEV)
     dw = torch.empty((N, K), dtype=torch.float32, device=DEV)

@@ -118,7 +118,7 @@ fp4q_status fp4q_quantize(const void* x, fp4q_dtype xt, int64_t rows, int64_t co
     if (layout == FP4Q_ROW16 && !codes_t) {
       const int64_t segs = (cols / 16 + 255) / 256;
       if (rows * segs > kMaxGridX) return FP4Q_E_SHAPE;
-    } else if (((cols / 8 + 255) / 256) * ((rows / 16 + 3) / 4) > kMaxGridX) {
+    } else if (((cols + 63) / 64) * ((rows + 63) / 64) > kMaxGridX) {
       return FP4Q_E_SHAPE;
     }
   }

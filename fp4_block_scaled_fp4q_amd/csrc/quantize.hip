@@ -181,11 +181,135 @@ __global__ __launch_bounds__(kThreads) void quant_row16_kernel(
 }
 
 // ------------------------------------------------------------------ ROW16 + COL16
-// A lane holds 8 consecutive columns and walks kSub sub-tiles of 16 rows
-// (64 rows for bf16, 32 for fp32). Column blocks (COL16) are complete inside
-// the lane, and the lane collects 8 * kSub contiguous bytes of each column's
-// codes before storing them; row blocks (ROW16) span the lane pair
-// (2t, 2t+1). Each element's Philox word serves both orientations.
+// A workgroup owns a 64 x 64 tile. Phase 1: thread t takes row t / 4 and 16
+// columns 16 (t % 4) .. +15 (one ROW16 block): coalesced loads, the ROW16
+// codes and scale when requested, and for SR the 16 Philox words; it parks
+// the raw inputs (and words) in LDS. Phase 2: thread t takes column t % 64
+// and rows 16 (t / 64) .. +15 (one COL16 block), reading LDS down the column
+// (a wave reads one LDS row, 64 consecutive elements: no bank conflicts),
+// and writes the COL16 codes and scale. Each element's Philox word serves
+// both orientations. Tiles are ordered so that one XCD runs the row tiles of
+// a column tile back to back (they fill the same lines of the COL16 codes).
+constexpr int kTT = 64;  // tile rows and columns
+
+template <bool kBF16, bool kSR, bool kRow>
+__global__ __launch_bounds__(kThreads) void quant_dual_kernel(
+    const uint8_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld_bytes, int col_tiles,
+    int row_tiles, const float* __restrict__ amax_held, float target, uint64_t seed,
+    uint32_t subseq, uint8_t* __restrict__ codes_r, uint8_t* __restrict__ scales_r,
+    uint8_t* __restrict__ codes_c, uint8_t* __restrict__ scales_c, float* __restrict__ enc_out,
+    int32_t* __restrict__ diag) {
+  constexpr int es = kBF16 ? 2 : 4;
+  constexpr int kXPitch = kTT * es + 16;  // bytes per LDS row of inputs (16 B pad)
+  constexpr int kWPitch = kTT * 4 + 16;   // bytes per LDS row of Philox words
+  __shared__ __attribute__((aligned(16))) uint8_t lx[kTT * kXPitch];
+  __shared__ __attribute__((aligned(16))) uint8_t lw[kSR ? kTT * kWPitch : 16];
+
+  const int item = xcd_order(blockIdx.x, col_tiles * row_tiles);
+  const int ct = item / row_tiles;
+  const int rt = item - ct * row_tiles;
+  const int64_t r0 = (int64_t)rt * kTT;
+  const int64_t c0 = (int64_t)ct * kTT;
+  const float S = tensor_scale(*amax_held, target);
+  const double S_d = (double)S;
+  if (enc_out && blockIdx.x == 0 && threadIdx.x == 0) *enc_out = S;
+  const int t = threadIdx.x;
+  uint32_t nzero = 0u, nsat = 0u;
+
+  // ---- phase 1: one row block per thread
+  {
+    const int r = t >> 2;
+    const int q = t & 3;
+    const int64_t gr = r0 + r;
+    const int64_t gc = c0 + 16 * q;
+    const bool vr = gr < rows;
+    const bool v0 = vr && gc < cols;
+    const bool v1 = vr && gc + 8 < cols;
+    Oct<kBF16> a, b;
+    if (v0) a.load(x + gr * ld_bytes + gc * es); else a.zero();
+    if (v1) b.load(x + gr * ld_bytes + (gc + 8) * es); else b.zero();
+    uint32_t w[16];
+    if (kSR) {
+      const uint64_t idx0 = (uint64_t)gr * (uint64_t)cols + (uint64_t)gc;
+      words8(idx0, seed, subseq, w);
+      words8(idx0 + 8, seed, subseq, w + 8);
+    }
+    if (kRow && v0) {  // cols % 16 == 0 here, so v0 implies v1
+      const BlockScale s = block_scale(max(a.absmax(), b.absmax()), S, S_d);
+      const bool mi = __builtin_isinf(s.mul);
+      const uint32_t lo = encode_oct<kBF16, kSR>(a, s.mul, mi, w);
+      const uint32_t hi = encode_oct<kBF16, kSR>(b, s.mul, mi, w + 8);
+      *reinterpret_cast<uint2*>(codes_r + gr * (cols / 2) + gc / 2) = make_uint2(lo, hi);
+      scales_r[gr * (cols / 16) + gc / 16] = (uint8_t)s.code;
+      nzero += s.flags & 1u;
+      nsat += s.flags >> 1;
+    }
+    uint4* dx = reinterpret_cast<uint4*>(lx + r * kXPitch + 16 * q * es);
+    if (kBF16) {
+      dx[0] = make_uint4(a.d[0], a.d[1], a.d[2], a.d[3]);
+      dx[1] = make_uint4(b.d[0], b.d[1], b.d[2], b.d[3]);
+    } else {
+      dx[0] = make_uint4(a.d[0], a.d[1], a.d[2], a.d[3]);
+      dx[1] = make_uint4(a.d[4], a.d[5], a.d[6], a.d[7]);
+      dx[2] = make_uint4(b.d[0], b.d[1], b.d[2], b.d[3]);
+      dx[3] = make_uint4(b.d[4], b.d[5], b.d[6], b.d[7]);
+    }
+    if (kSR) {
+      uint4* dw = reinterpret_cast<uint4*>(lw + r * kWPitch + 64 * q);
+#pragma clang loop unroll(full)
+      for (int k = 0; k < 4; ++k) dw[k] = make_uint4(w[4 * k], w[4 * k + 1], w[4 * k + 2], w[4 * k + 3]);
+    }
+  }
+  __syncthreads();
+
+  // ---- phase 2: one column block per thread
+  {
+    const int c = t & (kTT - 1);
+    const int rb = t >> 6;
+    const int64_t gc = c0 + c;
+    const int64_t gr0 = r0 + 16 * rb;
+    if (gc < cols && gr0 < rows) {
+      float v[16];
+      uint32_t m = 0u;
+#pragma clang loop unroll(full)
+      for (int r = 0; r < 16; ++r) {
+        const uint8_t* src = lx + (16 * rb + r) * kXPitch + c * es;
+        v[r] = kBF16 ? u2f((uint32_t)*reinterpret_cast<const uint16_t*>(src) << 16)
+                     : *reinterpret_cast<const float*>(src);
+        m = max(m, f2u(v[r]) & 0x7FFFFFFFu);
+      }
+      const BlockScale s = block_scale(m, S, S_d);
+      const bool mi = __builtin_isinf(s.mul);
+      uint32_t cw[2] = {0u, 0u};
+      if (__builtin_expect(mi, 0)) {
+#pragma clang loop unroll(full)
+        for (int r = 0; r < 16; ++r) cw[r >> 3] |= inf_code(v[r]) << (4 * (r & 7));
+      } else if (kSR) {
+#pragma clang loop unroll(full)
+        for (int r = 0; r < 16; ++r) {
+          const uint32_t wr = *reinterpret_cast<const uint32_t*>(lw + (16 * rb + r) * kWPitch + 4 * c);
+          cw[r >> 3] |= sr_code(v[r] * s.mul, wr) << (4 * (r & 7));
+        }
+      } else {
+        const float mu = s.mul;
+        cw[0] = FP4Q_ENC2(cw[0], v[0] * mu, v[1] * mu, 0);
+        cw[0] = FP4Q_ENC2(cw[0], v[2] * mu, v[3] * mu, 1);
+        cw[0] = FP4Q_ENC2(cw[0], v[4] * mu, v[5] * mu, 2);
+        cw[0] = FP4Q_ENC2(cw[0], v[6] * mu, v[7] * mu, 3);
+        cw[1] = FP4Q_ENC2(cw[1], v[8] * mu, v[9] * mu, 0);
+        cw[1] = FP4Q_ENC2(cw[1], v[10] * mu, v[11] * mu, 1);
+        cw[1] = FP4Q_ENC2(cw[1], v[12] * mu, v[13] * mu, 2);
+        cw[1] = FP4Q_ENC2(cw[1], v[14] * mu, v[15] * mu, 3);
+      }
+      *reinterpret_cast<uint2*>(codes_c + gc * (rows / 2) + gr0 / 2) = make_uint2(cw[0], cw[1]);
+      scales_c[gc * (rows / 16) + gr0 / 16] = (uint8_t)s.code;
+      nzero += s.flags & 1u;
+      nsat += s.flags >> 1;
+    }
+  }
+  if (diag) add_diag(diag, nzero, nsat);
+}
+
 template <bool kBF16>
 constexpr int sub_tiles() { return kBF16 ? 4 : 2; }
 
@@ -203,141 +327,6 @@ __device__ __forceinline__ void store_col_codes(uint8_t* dst, const uint32_t (&c
     for (int st = 0; st < kSub; ++st)
       if (st < nsub) reinterpret_cast<uint2*>(dst)[st] = make_uint2(cw[2 * st], cw[2 * st + 1]);
   }
-}
-
-template <bool kBF16, bool kSR, bool kRow, bool kCol>
-__global__ __launch_bounds__(kThreads) void quant_dual_kernel(
-    const uint8_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld_bytes, int col_groups,
-    int row_groups, const float* __restrict__ amax_held, float target, uint64_t seed,
-    uint32_t subseq, uint8_t* __restrict__ codes_r, uint8_t* __restrict__ scales_r,
-    uint8_t* __restrict__ codes_c, uint8_t* __restrict__ scales_c, float* __restrict__ enc_out,
-    int32_t* __restrict__ diag) {
-  constexpr int es = kBF16 ? 2 : 4;
-  constexpr int kSub = sub_tiles<kBF16>();
-  const int item = xcd_order(blockIdx.x, col_groups * row_groups);
-  const int cg = item / row_groups;
-  const int rg = item - cg * row_groups;
-  const float S = tensor_scale(*amax_held, target);
-  const double S_d = (double)S;
-  if (enc_out && blockIdx.x == 0 && threadIdx.x == 0) *enc_out = S;
-  const int64_t oct = (int64_t)cg * kThreads + threadIdx.x;
-  const int64_t c0 = oct * 8;
-  const bool valid = c0 < cols;  // for kRow equal within a lane pair (cols % 16 == 0)
-  const int64_t r_begin = (int64_t)rg * 16 * kSub;
-  const int nsub = (int)min((int64_t)kSub, (rows - r_begin) / 16);
-  const int half = threadIdx.x & 1;
-  uint32_t nzero = 0u, nsat = 0u;
-  uint32_t ccodes[8][2 * kSub];  // COL16 codes of column j, 16 * kSub rows
-  uint32_t cscale[8];            // COL16 scale codes of column j, one byte per sub-tile
-#pragma clang loop unroll(full)
-  for (int j = 0; j < 8; ++j) {
-    cscale[j] = 0u;
-#pragma clang loop unroll(full)
-    for (int q = 0; q < 2 * kSub; ++q) ccodes[j][q] = 0u;
-  }
-
-#pragma clang loop unroll(full)
-  for (int st = 0; st < kSub; ++st) {
-    if (st < nsub) {
-    const int64_t r0 = r_begin + st * 16;
-    Oct<kBF16> v[16];
-#pragma clang loop unroll(full)
-    for (int r = 0; r < 16; ++r) {
-      if (valid)
-        v[r].load(x + (r0 + r) * ld_bytes + c0 * es);
-      else
-        v[r].zero();
-    }
-    // COL16 block scales: one per column of this lane
-    BlockScale cs[8];
-    if (kCol) {
-#pragma clang loop unroll(full)
-      for (int j = 0; j < 8; ++j) {
-        uint32_t m = 0u;
-#pragma clang loop unroll(full)
-        for (int r = 0; r < 16; ++r) m = max(m, f2u(v[r].get(j)) & 0x7FFFFFFFu);
-        cs[j] = block_scale(m, S, S_d);
-        cscale[j] |= cs[j].code << (8 * st);
-        nzero += cs[j].flags & 1u;
-        nsat += cs[j].flags >> 1;
-      }
-    }
-    // ROW16 block scales: the even lane of a pair computes rows 0-7, the
-    // odd lane rows 8-15, and they swap multipliers
-    float rmul[16];
-    if (kRow) {
-      uint32_t rmax[16];
-#pragma clang loop unroll(full)
-      for (int r = 0; r < 16; ++r) {
-        const uint32_t m = v[r].absmax();
-        rmax[r] = max(m, (uint32_t)__shfl_xor((int)m, 1));
-      }
-#pragma clang loop unroll(full)
-      for (int k = 0; k < 8; ++k) {
-        const BlockScale b = block_scale(half ? rmax[8 + k] : rmax[k], S, S_d);
-        const float other = __shfl_xor(b.mul, 1);
-        rmul[k] = half ? other : b.mul;
-        rmul[8 + k] = half ? b.mul : other;
-        if (valid) scales_r[(r0 + 8 * half + k) * (cols / 16) + (oct >> 1)] = (uint8_t)b.code;
-        nzero += b.flags & 1u;
-        nsat += b.flags >> 1;
-      }
-    }
-    // payloads, row by row (pairs of rows for the RNE column codes)
-#pragma clang loop unroll(full)
-    for (int r = 0; r < 16; ++r) {
-      uint32_t w[8];
-      if (kSR) words8((uint64_t)(r0 + r) * (uint64_t)cols + (uint64_t)c0, seed, subseq, w);
-      if (kRow) {
-        const float mul = rmul[r];
-        const uint32_t word = encode_oct<kBF16, kSR>(v[r], mul, __builtin_isinf(mul), w);
-        if (valid) reinterpret_cast<uint32_t*>(codes_r + (r0 + r) * (cols / 2))[oct] = word;
-      }
-      if (kCol) {
-        const int q = 2 * st + (r >> 3);
-        if (kSR) {
-#pragma clang loop unroll(full)
-          for (int j = 0; j < 8; ++j) {
-            const uint32_t c = __builtin_isinf(cs[j].mul) ? inf_code(v[r].get(j))
-                                                          : sr_code(v[r].get(j) * cs[j].mul, w[j]);
-            ccodes[j][q] |= c << (4 * (r & 7));
-          }
-        } else if (r & 1) {
-          // rows r-1 and r of column j form one byte of the column code
-#pragma clang loop unroll(full)
-          for (int j = 0; j < 8; ++j) {
-            uint32_t byte;
-            if (__builtin_expect(__builtin_isinf(cs[j].mul), 0)) {
-              byte = inf_code(v[r - 1].get(j)) | (inf_code(v[r].get(j)) << 4);
-            } else {
-              byte = FP4Q_ENC2(0u, v[r - 1].get(j) * cs[j].mul, v[r].get(j) * cs[j].mul, 0) & 0xFFu;
-            }
-            ccodes[j][q] |= byte << (8 * ((r & 7) >> 1));
-          }
-        }
-      }
-    }
-    }  // st < nsub
-  }
-  if (kCol && valid && nsub > 0) {
-    const bool wide = (rows / 2) % 16 == 0;
-    const bool swide = (rows / 16) % kSub == 0 && nsub == kSub;
-#pragma clang loop unroll(full)
-    for (int j = 0; j < 8; ++j) {
-      store_col_codes<kSub>(codes_c + (c0 + j) * (rows / 2) + r_begin / 2, ccodes[j], nsub, wide);
-      uint8_t* sdst = scales_c + (c0 + j) * (rows / 16) + r_begin / 16;
-      if (swide && kSub == 4) {
-        *reinterpret_cast<uint32_t*>(sdst) = cscale[j];
-      } else if (swide && kSub == 2) {
-        *reinterpret_cast<uint16_t*>(sdst) = (uint16_t)cscale[j];
-      } else {
-#pragma clang loop unroll(full)
-        for (int st = 0; st < kSub; ++st)
-          if (st < nsub) sdst[st] = (uint8_t)(cscale[j] >> (8 * st));
-      }
-    }
-  }
-  if (diag) add_diag(diag, nzero, nsat);
 }
 
 // ------------------------------------------------------------------ TILE16
@@ -429,11 +418,11 @@ hipError_t launch_typed(const QuantArgs& a, hipStream_t s) {
                        a.scales, a.enc_scale_out, a.diag);
     return hipGetLastError();
   }
-  const int col_groups = (int)((a.cols / 8 + kThreads - 1) / kThreads);
-  constexpr int ksub = sub_tiles<kBF16>();
-  const int row_groups = (int)((a.rows / 16 + ksub - 1) / ksub);
-  const dim3 grid((uint32_t)(col_groups * row_groups));
   if (a.layout == 2) {
+    const int col_groups = (int)((a.cols / 8 + kThreads - 1) / kThreads);
+    constexpr int ksub = sub_tiles<kBF16>();
+    const int row_groups = (int)((a.rows / 16 + ksub - 1) / ksub);
+    const dim3 grid((uint32_t)(col_groups * row_groups));
     if (a.codes_t)
       hipLaunchKernelGGL((quant_tile_kernel<kBF16, kSR, true>), grid, dim3(kThreads), 0, s, x, a.rows,
                          a.cols, ldb, col_groups, row_groups, a.amax_held, a.target, a.seed, a.subseq,
@@ -442,15 +431,20 @@ hipError_t launch_typed(const QuantArgs& a, hipStream_t s) {
       hipLaunchKernelGGL((quant_tile_kernel<kBF16, kSR, false>), grid, dim3(kThreads), 0, s, x, a.rows,
                          a.cols, ldb, col_groups, row_groups, a.amax_held, a.target, a.seed, a.subseq,
                          a.codes, a.scales, nullptr, nullptr, a.enc_scale_out, a.diag);
-  } else if (both) {
+    return hipGetLastError();
+  }
+  const int col_tiles = (int)((a.cols + kTT - 1) / kTT);
+  const int row_tiles = (int)((a.rows + kTT - 1) / kTT);
+  const dim3 grid((uint32_t)(col_tiles * row_tiles));
+  if (both) {
     // ROW16 outputs in codes/scales, COL16 outputs in codes_t/scales_t
-    hipLaunchKernelGGL((quant_dual_kernel<kBF16, kSR, true, true>), grid, dim3(kThreads), 0, s, x,
-                       a.rows, a.cols, ldb, col_groups, row_groups, a.amax_held, a.target, a.seed,
-                       a.subseq, a.codes, a.scales, a.codes_t, a.scales_t, a.enc_scale_out, a.diag);
+    hipLaunchKernelGGL((quant_dual_kernel<kBF16, kSR, true>), grid, dim3(kThreads), 0, s, x, a.rows,
+                       a.cols, ldb, col_tiles, row_tiles, a.amax_held, a.target, a.seed, a.subseq,
+                       a.codes, a.scales, a.codes_t, a.scales_t, a.enc_scale_out, a.diag);
   } else {
-    hipLaunchKernelGGL((quant_dual_kernel<kBF16, kSR, false, true>), grid, dim3(kThreads), 0, s, x,
-                       a.rows, a.cols, ldb, col_groups, row_groups, a.amax_held, a.target, a.seed,
-                       a.subseq, nullptr, nullptr, a.codes, a.scales, a.enc_scale_out, a.diag);
+    hipLaunchKernelGGL((quant_dual_kernel<kBF16, kSR, false>), grid, dim3(kThreads), 0, s, x, a.rows,
+                       a.cols, ldb, col_tiles, row_tiles, a.amax_held, a.target, a.seed, a.subseq,
+                       nullptr, nullptr, a.codes, a.scales, a.enc_scale_out, a.diag);
   }
   return hipGetLastError();
 }

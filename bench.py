@@ -14,7 +14,7 @@ step of sample-and-hold tensor scaling:
   dW = dYq^T Xq    (fp32 out)    wgrad
 value = 3 * 2 M N K flops / step time (TFLOP/s); inputs are resident in HBM
 before timing starts. Also measured in the same run: each kernel's average
-duration (HIP events on the launch stream), the quantize-only workload
+duration inside the step (HIP events on the launch stream), the quantize-only workload
 (8192x4096 bf16 ROW16 RNE, rotating over >256 MiB of inputs so the Infinity
 Cache cannot serve it) in GB/s, and the CPU oracle on a bounded sample.
 Prints one JSON line.
@@ -42,7 +42,6 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--kernel-reps", type=int, default=10)
     ap.add_argument("--quiet", action="store_true")
     ap.add_argument("--profile-op", default=None,
                     help="profiling mode: run only this launch of the step (e.g. gemm_fwd, "
@@ -141,37 +140,42 @@ def main():
     value = flops_step / (ms_per_step * 1e-3) / 1e12
     log(args, f"timed {args.steps} steps: {ms_per_step:.3f} ms/step, {value:.1f} TFLOP/s")
 
-    # per-kernel average durations (events bracketing kernel_reps launches)
-    kern = {}
-    for name, fn in ops:
-        if name in kern:
-            continue
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        fn()
-        a.record()
-        for _ in range(args.kernel_reps):
+    # per-kernel durations inside the step: a second pass of the same steps with
+    # a HIP event recorded on the launch stream between consecutive launches
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(ops) + 1)]
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for s_ev in evs:
+        s_ev[0].record()
+        for i, (_, fn) in enumerate(ops):
             fn()
-        b.record()
-        torch.cuda.synchronize()
-        kern[name] = a.elapsed_time(b) / args.kernel_reps * 1e3  # us per call
-    log(args, "per-call us: " + ", ".join(f"{k}={v:.1f}" for k, v in kern.items()))
+            s_ev[i + 1].record()
+    torch.cuda.synchronize()
+    fam_us, fam_calls = {}, {}
+    for s_ev in evs:
+        for i, (name, _) in enumerate(ops):
+            fam_us[name] = fam_us.get(name, 0.0) + s_ev[i].elapsed_time(s_ev[i + 1]) * 1e3
+            fam_calls[name] = fam_calls.get(name, 0) + 1
+    kern = {k: fam_us[k] / fam_calls[k] for k in fam_us}  # us per call
+    log(args, "per-call us in the step: " + ", ".join(f"{k}={v:.1f}" for k, v in kern.items()))
 
     gemm_us = (kern["gemm_fwd"] + kern["gemm_dgrad"] + kern["gemm_wgrad"]) / 3.0
     gemm_tflops = 2.0 * M * N * K / (gemm_us * 1e-6) / 1e12
 
-    # algorithmic bytes of each codec launch (read once + write once)
+    # algorithmic bytes of each codec launch family per step (each input read
+    # once, each output written once)
     def qbytes(rows, cols, es, transposed=False):
         b = rows * cols * es + rows * cols / 2 + rows * cols / 16
         if transposed:
             b += rows * cols / 2 + rows * cols / 256
         return b
     codec_bytes = {
-        "amax": (M * K + N * K + M * N) * 2 / 3.0,  # average of the three launches
+        "amax": (M * K + N * K + M * N) * 2,  # the three launches together
         "quant_x_row_col": qbytes(M, K, 2) + M * K * (0.5 + 1 / 16),
         "quant_w_tile": qbytes(N, K, 2, True) - N * K / 16 + N * K / 256,
         "quant_dy_row_col_sr": qbytes(M, N, 2) + M * N * (0.5 + 1 / 16),
     }
-    codec_gbs = {k: codec_bytes[k] / (kern[k] * 1e-6) / 1e9 for k in codec_bytes}
+    codec_gbs = {k: codec_bytes[k] * args.steps / (fam_us[k] * 1e-6) / 1e9 for k in codec_bytes}
 
     # quantize-only workload: 8192x4096 bf16 ROW16 RNE, held amax, rotated inputs
     qw = inputs.make("quantize", with_held=True)
@@ -295,7 +299,7 @@ def cpu_baseline(args, wl, M, N, K):
     import oracle
     from threadpoolctl import threadpool_info
 
-    Ms = 128
+    Ms = 2048
     Xs = wl.tensors["X"].oracle_view[:Ms]
     dYs = wl.tensors["dY"].oracle_view[:Ms]
     Wv = wl.tensors["W"].oracle_view

@@ -190,14 +190,28 @@ def main():
     for i in range(nrot):
         api.fp4q_quantize(Xrot[i], held, T, api.ROW16, api.RNE, 0, 0, qc, qs, qS)
     reps = 5 * nrot
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # The launches are replayed from a HIP graph: a kernel this short would
+    # otherwise wait on the Python-side launch of the next one.
     torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        for i in range(reps):
+            api.fp4q_quantize(Xrot[i % nrot], held, T, api.ROW16, api.RNE, 0, 0, qc, qs, qS)
+    graph.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record()
-    for i in range(reps):
-        api.fp4q_quantize(Xrot[i % nrot], held, T, api.ROW16, api.RNE, 0, 0, qc, qs, qS)
+    graph.replay()
     b.record()
     torch.cuda.synchronize()
     q_us = a.elapsed_time(b) / reps * 1e3
+    # the replayed result equals an eager call on the same (last) input
+    ec, es_ = torch.empty_like(qc), torch.empty_like(qs)
+    api.fp4q_quantize(Xrot[(reps - 1) % nrot], held, T, api.ROW16, api.RNE, 0, 0, ec, es_, qS)
+    torch.cuda.synchronize()
+    if not (torch.equal(ec, qc) and torch.equal(es_, qs)):
+        raise RuntimeError("quantize replayed from a graph differs from the eager call")
     q_bytes = Mq * Kq * (2 + 0.5 + 1 / 16)
     q_gbs = q_bytes / (q_us * 1e-6) / 1e9
     del Xrot

@@ -116,7 +116,7 @@ fp4q_status fp4q_quantize(const void* x, fp4q_dtype xt, int64_t rows, int64_t co
     if (!aligned(x, 16) || (ld * es) % 16) return FP4Q_E_ALIGN;
     if (!aligned(codes, 8) || (codes_t && !aligned(codes_t, 8))) return FP4Q_E_ALIGN;
     if (layout == FP4Q_ROW16 && !codes_t) {
-      const int64_t segs = (cols / 16 + 255) / 256;
+      const int64_t segs = (cols / 16 + 63) / 64;
       if (rows * segs > kMaxGridX) return FP4Q_E_SHAPE;
     } else if (((cols + 63) / 64) * ((rows + 63) / 64) > kMaxGridX) {
       return FP4Q_E_SHAPE;

@@ -42,7 +42,9 @@ __device__ __forceinline__ float half_bits_to_float(uint32_t bits16) {
 
 __device__ __forceinline__ float ue5m3_value(uint32_t code) { return half_bits_to_float(code << 7); }
 
-// 16-byte streaming load (read once, do not keep in cache).
+// 16-byte loads. The quantize kernels use plain loads; the amax reduction
+// (a pure read stream) measured faster with the nontemporal form.
+__device__ __forceinline__ uint4 load16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ uint4 load_nt16(const void* p) {
   const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
@@ -132,9 +134,9 @@ __device__ __forceinline__ uint32_t sr_code(float v, uint32_t w) {
   const uint32_t ea = f2u(a2) >> 23;
   const uint32_t e = min(max(ea, 128u), 130u) - 128u;
   const float b = __builtin_ldexpf(a2, -(int)e);
-  const float fl = __builtin_floorf(b);
-  const uint32_t t = (uint32_t)__builtin_ceilf((b - fl) * 4294967296.0f);
-  const uint32_t mag = 2u * e + (uint32_t)fl + (w < t ? 1u : 0u);
+  // fract(B) = B - floor(B) exactly for B >= 0; truncation gives floor(B)
+  const uint32_t t = (uint32_t)__builtin_ceilf(__builtin_amdgcn_fractf(b) * 4294967296.0f);
+  const uint32_t mag = 2u * e + (uint32_t)b + (w < t ? 1u : 0u);
   return ((u >> 28) & 8u) | mag;
 }
 
@@ -161,9 +163,9 @@ __device__ __forceinline__ U4 philox4x32_10(U4 c, uint32_t k0, uint32_t k1) {
     const uint32_t hi0 = (uint32_t)(p0 >> 32), lo0 = (uint32_t)p0;
     const uint32_t hi1 = (uint32_t)(p1 >> 32), lo1 = (uint32_t)p1;
     U4 n;
-    n.x = hi1 ^ c.y ^ k0;
+    n.x = __builtin_amdgcn_bitop3_b32(hi1, c.y, k0, 0x96);  // three-way xor
     n.y = lo1;
-    n.z = hi0 ^ c.w ^ k1;
+    n.z = __builtin_amdgcn_bitop3_b32(hi0, c.w, k1, 0x96);
     n.w = lo0;
     c = n;
     k0 += 0x9E3779B9u;

@@ -275,11 +275,37 @@ __global__ __launch_bounds__(64 * kWavesM * kWavesN) void gemm_kernel(
     __syncthreads();
   }
 
-  // epilogue: y = acc * alpha, alpha = 1 / (Sa Sb)
+  // epilogue: y = acc * alpha, alpha = 1 / (Sa Sb). Interior tiles (and a
+  // normal fp32 alpha) take a branch-free path: a uniform tile base plus
+  // 32-bit in-tile offsets, two rows per step.
   const double alpha_d = 1.0 / ((double)*a_S * (double)*b_S);
   const float alpha = (float)alpha_d;
   const bool alpha_normal = alpha >= 1.17549435e-38f && alpha <= 3.40282347e+38f;
+  constexpr int es = kF32Out ? 4 : 2;
   const bool full_tile = m0 + BM <= M && n0 + BN <= N;
+  if (full_tile && alpha_normal && N * es * BM < 0xFFFFFFFFll) {
+    char* tile_base = static_cast<char*>(y) + (m0 * N + n0) * es;
+    const uint32_t lane_off = (uint32_t)(((wm * kTM + 4 * hi) * N + wn * kTN + (lane & 31)) * es);
+#pragma unroll
+    for (int i = 0; i < kFM; ++i)
+#pragma unroll
+      for (int j = 0; j < kFN; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; e += 2) {
+          const uint32_t r0 = (uint32_t)(i * 32 + 8 * (e >> 2) + (e & 3));
+          const uint32_t o0 = lane_off + (uint32_t)((r0 * N + j * 32) * es);
+          const uint32_t o1 = o0 + (uint32_t)(N * es);
+          const float v0 = acc[i][j][e] * alpha, v1 = acc[i][j][e + 1] * alpha;
+          if (kF32Out) {
+            *reinterpret_cast<float*>(tile_base + o0) = v0;
+            *reinterpret_cast<float*>(tile_base + o1) = v1;
+          } else {
+            *reinterpret_cast<__bf16*>(tile_base + o0) = (__bf16)v0;
+            *reinterpret_cast<__bf16*>(tile_base + o1) = (__bf16)v1;
+          }
+        }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < kFM; ++i)
 #pragma unroll
@@ -289,7 +315,7 @@ __global__ __launch_bounds__(64 * kWavesM * kWavesN) void gemm_kernel(
       for (int e = 0; e < 16; ++e) {
         const int64_t r = m0 + wm * kTM + i * 32 + 8 * (e >> 2) + 4 * hi + (e & 3);
         const float v = alpha_normal ? acc[i][j][e] * alpha : (float)((double)acc[i][j][e] * alpha_d);
-        if (full_tile || (r < M && c < N)) {
+        if (r < M && c < N) {
           if (kF32Out) {
             static_cast<float*>(y)[r * N + c] = v;
           } else {

@@ -41,7 +41,7 @@ template <>
 struct Oct<true> {
   uint32_t d[4];
   __device__ __forceinline__ void load(const uint8_t* p) {
-    const uint4 v = load_nt16(p);
+    const uint4 v = load16(p);
     d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
   }
   __device__ __forceinline__ void zero() { d[0] = d[1] = d[2] = d[3] = 0u; }
@@ -58,8 +58,8 @@ template <>
 struct Oct<false> {
   uint32_t d[8];
   __device__ __forceinline__ void load(const uint8_t* p) {
-    const uint4 a = load_nt16(p);
-    const uint4 b = load_nt16(p + 16);
+    const uint4 a = load16(p);
+    const uint4 b = load16(p + 16);
     d[0] = a.x; d[1] = a.y; d[2] = a.z; d[3] = a.w;
     d[4] = b.x; d[5] = b.y; d[6] = b.z; d[7] = b.w;
   }
@@ -140,10 +140,13 @@ __device__ __forceinline__ int xcd_order(int L, int n) {
 }
 
 // ------------------------------------------------------------------ ROW16
-// One 16-element block per lane (two Octs). A workgroup covers kThreads
-// consecutive blocks of one row.
+// One 16-element block per lane (two Octs). A workgroup (one wave) covers
+// kRowThreads consecutive blocks of one row; small workgroups measured
+// fastest for this stream.
+constexpr int kRowThreads = 64;
+
 template <bool kBF16, bool kSR>
-__global__ __launch_bounds__(kThreads) void quant_row16_kernel(
+__global__ __launch_bounds__(kRowThreads) void quant_row16_kernel(
     const uint8_t* __restrict__ x, int64_t cols, int64_t ld_bytes, int segs_per_row,
     const float* __restrict__ amax_held, float target, uint64_t seed, uint32_t subseq,
     uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, float* __restrict__ enc_out,
@@ -155,7 +158,7 @@ __global__ __launch_bounds__(kThreads) void quant_row16_kernel(
   const double S_d = (double)S;
   if (enc_out && blockIdx.x == 0 && threadIdx.x == 0) *enc_out = S;
   const int64_t nblk = cols / 16;
-  const int64_t blk = (int64_t)seg * kThreads + threadIdx.x;
+  const int64_t blk = (int64_t)seg * kRowThreads + threadIdx.x;
   uint32_t nzero = 0u, nsat = 0u;
   if (blk < nblk) {
     const uint8_t* p = x + row * ld_bytes + blk * 16 * es;
@@ -412,8 +415,8 @@ hipError_t launch_typed(const QuantArgs& a, hipStream_t s) {
   const bool both = a.layout == 0 && a.codes_t != nullptr;
   if (a.layout == 0 && !both) {
     const int64_t nblk = a.cols / 16;
-    const int segs = (int)((nblk + kThreads - 1) / kThreads);
-    hipLaunchKernelGGL((quant_row16_kernel<kBF16, kSR>), dim3((uint32_t)(a.rows * segs)), dim3(kThreads),
+    const int segs = (int)((nblk + kRowThreads - 1) / kRowThreads);
+    hipLaunchKernelGGL((quant_row16_kernel<kBF16, kSR>), dim3((uint32_t)(a.rows * segs)), dim3(kRowThreads),
                        0, s, x, a.cols, ldb, segs, a.amax_held, a.target, a.seed, a.subseq, a.codes,
                        a.scales, a.enc_scale_out, a.diag);
     return hipGetLastError();

@@ -121,7 +121,8 @@ def main():
             fn()
 
     if args.profile_op:
-        profile_only(args, ops, X, dev, api, inputs, torch)
+        extra = {"gemm_probe_fwd": lambda: api.fp4q_linear_probe(xq, wq, Y, 10)}
+        profile_only(args, ops, X, dev, api, inputs, torch, extra)
         return
 
     for _ in range(args.warmup):
@@ -176,6 +177,18 @@ def main():
         "quant_dy_row_col_sr": qbytes(M, N, 2) + M * N * (0.5 + 1 / 16),
     }
     codec_gbs = {k: codec_bytes[k] * args.steps / (fam_us[k] * 1e-6) / 1e9 for k in codec_bytes}
+
+    # the probe-matched accumulation mode on the forward GEMM (same operands)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    api.fp4q_linear_probe(xq, wq, Y, 10)
+    a.record()
+    for _ in range(3):
+        api.fp4q_linear_probe(xq, wq, Y, 10)
+    b.record()
+    torch.cuda.synchronize()
+    probe_us = a.elapsed_time(b) / 3 * 1e3
+    probe_tflops = 2.0 * M * N * K / (probe_us * 1e-6) / 1e12
+    log(args, f"probe-mode fwd GEMM: {probe_us:.1f} us, {probe_tflops:.1f} TFLOP/s")
 
     # quantize-only workload: 8192x4096 bf16 ROW16 RNE, held amax, rotated inputs
     qw = inputs.make("quantize", with_held=True)
@@ -258,11 +271,17 @@ def main():
         "quantize_only": {"workload": "8192x4096 bf16 ROW16 RNE, held amax", "us": round(q_us, 2),
                           "GB/s": round(q_gbs, 1), "frac_hbm": round(q_gbs / HBM_PEAK_GBS, 4)},
         "cpu_baseline": cpu,
+        "next_rows": {
+            "probe_gemm_fwd": {"what": "fwd GEMM with the probe-matched accumulation (64-wide slices, "
+                                       "toward-zero slice additions, 1/1024 snap)",
+                               "us": round(probe_us, 1), "TFLOP/s": round(probe_tflops, 1),
+                               "frac_bf16_peak": round(probe_tflops / BF16_PEAK_TFLOPS, 4)},
+        },
     }
     print(json.dumps(out), flush=True)
 
 
-def profile_only(args, ops, X, dev, api, inputs, torch):
+def profile_only(args, ops, X, dev, api, inputs, torch, extra):
     """Run each launch kind of a comma-separated --profile-op list --reps
     times (after one untimed call), for counter collection and tuning.
     'quantize_only' is the 8192x4096 ROW16 RNE workload; 'copy' is a plain
@@ -290,7 +309,7 @@ def profile_only(args, ops, X, dev, api, inputs, torch):
                     if not k.startswith("gemm"):
                         f()  # the operands the measured launches read
                 prepared = True
-            fn = dict(ops)[name]
+            fn = extra[name] if name in extra else dict(ops)[name]
         fn()
         torch.cuda.synchronize()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)

@@ -22,7 +22,7 @@ ROW16, COL16, TILE16x16 = 0, 1, 2
 
 # every entry point include/fp4q.h declares
 EXPORTS = ("fp4q_abi_version", "fp4q_status_str", "fp4q_amax", "fp4q_quantize", "fp4q_dequant",
-           "fp4q_linear_fwd", "fp4q_linear_dgrad", "fp4q_linear_wgrad")
+           "fp4q_linear_fwd", "fp4q_linear_dgrad", "fp4q_linear_wgrad", "fp4q_linear_probe")
 
 
 class QTensorC(ctypes.Structure):
@@ -67,6 +67,8 @@ def lib() -> ctypes.CDLL:
         fn = getattr(L, name)
         fn.restype = ctypes.c_int
         fn.argtypes = [qp, qp, p, ctypes.c_int, p]
+    L.fp4q_linear_probe.restype = ctypes.c_int
+    L.fp4q_linear_probe.argtypes = [qp, qp, p, ctypes.c_int, ctypes.c_int32, p]
     _lib = L
     return L
 

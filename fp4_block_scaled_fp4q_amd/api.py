@@ -116,6 +116,19 @@ def fp4q_linear_wgrad(dyqt: QTensor, xqt: QTensor, dw: torch.Tensor) -> None:
     _gemm("fp4q_linear_wgrad", dyqt, xqt, dw)
 
 
+def fp4q_linear_probe(a: QTensor, b: QTensor, y: torch.Tensor, snap_log2: int = 0) -> None:
+    """y[M, N] = A . B^T with the probe-matched accumulation (64-wide slices,
+    round-toward-zero addition of the slice sums, optional snap to multiples
+    of 2^-snap_log2)."""
+    if not y.is_contiguous():
+        raise ValueError("fp4q_linear_probe: output must be contiguous")
+    if tuple(y.shape) != (a.rows, b.rows):
+        raise ValueError(f"fp4q_linear_probe: output shape {tuple(y.shape)} != {(a.rows, b.rows)}")
+    ac, bc = a.c(), b.c()
+    check("fp4q_linear_probe", lib().fp4q_linear_probe(ac, bc, y.data_ptr(), _dtype_code(y), int(snap_log2),
+                                                       _stream()))
+
+
 # ---------------------------------------------------------------- helpers
 def amax(x: torch.Tensor) -> torch.Tensor:
     out = torch.empty(1, dtype=torch.float32, device=x.device)

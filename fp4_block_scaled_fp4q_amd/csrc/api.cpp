@@ -43,7 +43,7 @@ fp4q::QOperand to_operand(const fp4q_qtensor* q) {
 }
 
 fp4q_status gemm(const fp4q_qtensor* a, const fp4q_qtensor* b, void* y, fp4q_dtype yt,
-                 void* stream) {
+                 void* stream, bool probe = false, int snap_log2 = 0) {
   fp4q_status st = check_operand(a);
   if (st != FP4Q_OK) return st;
   st = check_operand(b);
@@ -52,7 +52,10 @@ fp4q_status gemm(const fp4q_qtensor* a, const fp4q_qtensor* b, void* y, fp4q_dty
   if (!es) return FP4Q_E_DTYPE;
   if (a->cols != b->cols) return FP4Q_E_SHAPE;
   if (a->rows > 0 && b->rows > 0 && !y) return FP4Q_E_NULL;
-  if (((a->rows + 255) / 256) * ((b->rows + 255) / 256) > 0x7FFFFFFF / 512) return FP4Q_E_SHAPE;
+  if (((a->rows + 127) / 128) * ((b->rows + 127) / 128) > 0x7FFFFFFF / 512) return FP4Q_E_SHAPE;
+  if (probe)
+    return from_hip(fp4q::launch_gemm_probe(to_operand(a), to_operand(b), y, es, snap_log2,
+                                            static_cast<hipStream_t>(stream)));
   return from_hip(fp4q::launch_gemm(to_operand(a), to_operand(b), y, es,
                                     static_cast<hipStream_t>(stream)));
 }
@@ -171,6 +174,12 @@ fp4q_status fp4q_linear_dgrad(const fp4q_qtensor* dyq, const fp4q_qtensor* wqt, 
 fp4q_status fp4q_linear_wgrad(const fp4q_qtensor* dyqt, const fp4q_qtensor* xqt, void* dw,
                               fp4q_dtype dwt, void* stream) {
   return gemm(dyqt, xqt, dw, dwt, stream);
+}
+
+fp4q_status fp4q_linear_probe(const fp4q_qtensor* a, const fp4q_qtensor* b, void* y,
+                              fp4q_dtype yt, int32_t snap_log2, void* stream) {
+  if (snap_log2 < 0 || snap_log2 > 30) return FP4Q_E_ARG;
+  return gemm(a, b, y, yt, stream, true, snap_log2);
 }
 
 }  // extern "C"

@@ -38,7 +38,7 @@ def build(force: bool = True) -> str:
     """Compile the oracle with gcc (plain IEEE binary32, no FMA contraction)."""
     if force or not os.path.exists(_LIB):
         tmp = _LIB + ".tmp"
-        cmd = ["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math",
+        cmd = ["gcc", "-O2", "-std=gnu11", "-ffp-contract=off", "-fno-fast-math", "-frounding-math",
                "-fPIC", "-shared", "-o", tmp, _SRC, "-lm"]
         subprocess.run(cmd, check=True)
         os.replace(tmp, _LIB)
@@ -84,6 +84,8 @@ def lib():
         L.oracle_dequant_f32.argtypes = [c_p, c_p, c_i64, c_i64, ctypes.c_int, c_f, c_p]
         L.oracle_gemm_f64_loops.restype = None
         L.oracle_gemm_f64_loops.argtypes = [c_p, c_p, c_i64, c_i64, c_i64, c_d, c_d, c_p]
+        L.oracle_gemm_probe.restype = ctypes.c_int
+        L.oracle_gemm_probe.argtypes = [c_p, c_p, c_i64, c_i64, c_i64, c_f, c_f, ctypes.c_int, c_p]
         _lib = L
     return _lib
 
@@ -244,6 +246,38 @@ def gemm(a: QTensor, b: QTensor) -> np.ndarray:
     A = decode_f64(a)
     B = decode_f64(b)
     return (A @ B.T) / (np.float64(a.S) * np.float64(b.S))
+
+
+def gemm_probe(a: QTensor, b: QTensor, snap_log2: int = 0) -> np.ndarray:
+    """The probe-matched GEMM numerics ("UE5M3 FP4 Block Scaling ...", §6 and
+    Appendix B): exact 64-wide slice dot products rounded once to binary32,
+    slice partials added in order with binary32 additions rounded toward
+    zero, an optional snap of the accumulator to multiples of 2^-snap_log2
+    (ties to even), then the binary32 product with alpha = 1 / (Sa Sb).
+    Returns float32 [a.rows, b.rows]."""
+    if a.cols != b.cols:
+        raise ValueError("contraction lengths differ")
+    A = np.ascontiguousarray(decode_f64(a))
+    B = np.ascontiguousarray(decode_f64(b))
+    y = np.zeros((a.rows, b.rows), np.float32)
+    rc = lib().oracle_gemm_probe(_ptr(A), _ptr(B), a.rows, b.rows, a.cols, float(a.S), float(b.S),
+                                 int(snap_log2), _ptr(y))
+    if rc != 0:
+        raise ValueError("decoded operand off the 2^-18 lattice")
+    return y
+
+
+def gemm_probe_decoded(A: np.ndarray, B: np.ndarray, Sa: float = 1.0, Sb: float = 1.0,
+                       snap_log2: int = 0) -> np.ndarray:
+    """gemm_probe on already decoded float64 operands (multiples of 2^-18)."""
+    A = np.ascontiguousarray(A, np.float64)
+    B = np.ascontiguousarray(B, np.float64)
+    y = np.zeros((A.shape[0], B.shape[0]), np.float32)
+    rc = lib().oracle_gemm_probe(_ptr(A), _ptr(B), A.shape[0], B.shape[0], A.shape[1], float(Sa),
+                                 float(Sb), int(snap_log2), _ptr(y))
+    if rc != 0:
+        raise ValueError("decoded operand off the 2^-18 lattice")
+    return y
 
 
 def gemm_loops(a: QTensor, b: QTensor) -> np.ndarray:

@@ -21,6 +21,8 @@
  *            Pseudo-Quantization Training"
  * Readings taken where the pages are silent are marked READING.
  */
+#include <fenv.h>
+#include <float.h>
 #include <math.h>
 #include <stdint.h>
 #include <string.h>
@@ -467,4 +469,78 @@ void oracle_gemm_f64_loops(const double *a, const double *b, int64_t m, int64_t 
                 acc += a[i * k + t] * b[j * k + t];
             y[i * n + j] = acc / (sa * sb);
         }
+}
+
+/*
+ * Probe-matched GEMM numerics ([UE5M3] §6 and Appendix B: the page's model
+ * of native FP4 GEMM outputs). For each output element the contraction is
+ * cut into consecutive slices of 64 along K; each slice's dot product of the
+ * decoded operands is formed exactly and rounded once to binary32; the slice
+ * partials are added in ascending slice order with binary32 additions
+ * rounded toward zero; optionally the accumulator is snapped to the nearest
+ * multiple of 2^-snap_log2 (ties to even: 1024 * c rounded, divided by 1024
+ * for snap_log2 = 10); then it is multiplied by the tensor-scale product.
+ * READING: the slice sum is rounded to nearest (once), the first partial
+ * starts the sum, alpha = 1 / (Sa Sb) is formed in double and applied as one
+ * binary32 multiply when it is a normal binary32 (else the product is formed
+ * in double and rounded once), a shorter last slice when K % 64 != 0.
+ *
+ * Decoded operands (e2m1 * scale) are multiples of 2^-18 below 2^19, so
+ * each is an integer n * 2^-18 with |n| < 2^37 and the slice sums are exact
+ * in 128-bit integers (|sum| < 64 * 2^74).
+ */
+static float i128_scaled_rn(__int128 s, int e)
+{
+    if (s == 0) return 0.0f;
+    const int neg = s < 0;
+    const unsigned __int128 u = neg ? -(unsigned __int128)s : (unsigned __int128)s;
+    int top = 0;
+    for (unsigned __int128 t = u; t > 1; t >>= 1) ++top;
+    uint64_t kept;
+    int sh = 0;
+    if (top <= 23) {
+        kept = (uint64_t)u;
+    } else {
+        sh = top - 23;
+        const unsigned __int128 one = 1;
+        const unsigned __int128 rem = u & ((one << sh) - 1);
+        const unsigned __int128 half = one << (sh - 1);
+        kept = (uint64_t)(u >> sh);
+        if (rem > half || (rem == half && (kept & 1u))) ++kept; /* ties to even */
+    }
+    const float f = ldexpf((float)kept, sh + e); /* kept <= 2^24: exact */
+    return neg ? -f : f;
+}
+
+int oracle_gemm_probe(const double *a, const double *b, int64_t m, int64_t n, int64_t k,
+                      float sa, float sb, int snap_log2, float *y)
+{
+    const double unit = 262144.0; /* 2^18 */
+    const double alpha_d = 1.0 / ((double)sa * (double)sb);
+    const float alpha = (float)alpha_d;
+    const int alpha_normal = alpha >= FLT_MIN && alpha <= FLT_MAX;
+    const int prev = fegetround();
+    for (int64_t i = 0; i < m; ++i)
+        for (int64_t j = 0; j < n; ++j) {
+            float acc = 0.0f;
+            for (int64_t g0 = 0; g0 < k; g0 += 64) {
+                const int64_t g1 = g0 + 64 < k ? g0 + 64 : k;
+                __int128 sum = 0;
+                for (int64_t t = g0; t < g1; ++t) {
+                    const double va = a[i * k + t] * unit, vb = b[j * k + t] * unit;
+                    const int64_t na = (int64_t)va, nb = (int64_t)vb;
+                    if ((double)na != va || (double)nb != vb) return 1; /* not on the lattice */
+                    sum += (__int128)na * (__int128)nb;
+                }
+                const float p = i128_scaled_rn(sum, -36);
+                fesetround(FE_TOWARDZERO);
+                volatile float t = acc + p;
+                acc = t;
+                fesetround(FE_TONEAREST);
+            }
+            if (snap_log2 > 0) acc = ldexpf(nearbyintf(ldexpf(acc, snap_log2)), -snap_log2);
+            y[i * n + j] = alpha_normal ? acc * alpha : (float)((double)acc * alpha_d);
+        }
+    fesetround(prev);
+    return 0;
 }

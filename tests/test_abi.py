@@ -101,3 +101,14 @@ def test_gemm_and_dequant_validation():
     assert L.fp4q_dequant(q(32, 64), None, _lib.F32, None) == _lib.E_NULL
     assert L.fp4q_dequant(q(32, 64), FAKE_ODD, _lib.F32, None) == _lib.E_ALIGN
     assert L.fp4q_dequant(q(32, 64), FAKE, 9, None) == _lib.E_DTYPE
+
+
+def test_probe_gemm_validation():
+    L = _lib.lib()
+    a, b = q(32, 64), q(48, 64, _lib.TILE16x16)
+    assert L.fp4q_linear_probe(a, b, FAKE, _lib.F32, -1, None) == _lib.E_ARG
+    assert L.fp4q_linear_probe(a, b, FAKE, _lib.F32, 31, None) == _lib.E_ARG
+    assert L.fp4q_linear_probe(None, b, FAKE, _lib.F32, 0, None) == _lib.E_NULL
+    assert L.fp4q_linear_probe(a, q(48, 80, _lib.TILE16x16), FAKE, _lib.F32, 10, None) == _lib.E_SHAPE
+    assert L.fp4q_linear_probe(a, b, FAKE, 7, 10, None) == _lib.E_DTYPE
+    assert L.fp4q_linear_probe(a, b, None, _lib.BF16, 10, None) == _lib.E_NULL

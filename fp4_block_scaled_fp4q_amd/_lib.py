@@ -19,17 +19,20 @@ OK, E_NULL, E_SHAPE, E_ALIGN, E_DTYPE, E_ARG, E_HIP = range(7)
 F32, BF16 = 0, 1
 RNE, SR = 0, 1
 ROW16, COL16, TILE16x16 = 0, 1, 2
+UE5M3, E4M3 = 0, 1
 
 # every entry point include/fp4q.h declares
-EXPORTS = ("fp4q_abi_version", "fp4q_status_str", "fp4q_amax", "fp4q_quantize", "fp4q_dequant",
-           "fp4q_linear_fwd", "fp4q_linear_dgrad", "fp4q_linear_wgrad", "fp4q_linear_probe")
+EXPORTS = ("fp4q_abi_version", "fp4q_status_str", "fp4q_amax", "fp4q_quantize", "fp4q_quantize_fmt",
+           "fp4q_dequant", "fp4q_linear_fwd", "fp4q_linear_dgrad", "fp4q_linear_wgrad",
+           "fp4q_linear_probe")
 
 
 class QTensorC(ctypes.Structure):
     """fp4q_qtensor."""
     _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p),
                 ("enc_scale", ctypes.c_void_p), ("rows", ctypes.c_int64),
-                ("cols", ctypes.c_int64), ("layout", ctypes.c_int32)]
+                ("cols", ctypes.c_int64), ("layout", ctypes.c_int32), ("block", ctypes.c_int32),
+                ("scale_fmt", ctypes.c_int32)]
 
 
 class Fp4qError(RuntimeError):
@@ -61,6 +64,9 @@ def lib() -> ctypes.CDLL:
     L.fp4q_quantize.restype = ctypes.c_int
     L.fp4q_quantize.argtypes = [p, ctypes.c_int, i64, i64, i64, p, f, ctypes.c_int, ctypes.c_int,
                                 u64, u32, p, p, p, p, p, p, p]
+    L.fp4q_quantize_fmt.restype = ctypes.c_int
+    L.fp4q_quantize_fmt.argtypes = [p, ctypes.c_int, i64, i64, i64, p, f, ctypes.c_int, i32, ctypes.c_int,
+                                    ctypes.c_int, u64, u32, p, p, p, p, p, p, p]
     L.fp4q_dequant.restype = ctypes.c_int
     L.fp4q_dequant.argtypes = [qp, p, ctypes.c_int, p]
     for name in ("fp4q_linear_fwd", "fp4q_linear_dgrad", "fp4q_linear_wgrad"):

@@ -13,11 +13,13 @@ from dataclasses import dataclass
 import torch
 
 from . import _lib
-from ._lib import BF16, COL16, F32, QTensorC, RNE, ROW16, SR, TILE16x16, check, lib
+from ._lib import (BF16, COL16, E4M3, F32, QTensorC, RNE, ROW16, SR, TILE16x16, UE5M3, check,
+                   lib)
 
-__all__ = ["QTensor", "fp4q_amax", "fp4q_quantize", "fp4q_dequant", "fp4q_linear_fwd",
-           "fp4q_linear_dgrad", "fp4q_linear_wgrad", "quantize", "amax", "dequant",
-           "ROW16", "COL16", "TILE16x16", "RNE", "SR", "F32", "BF16"]
+__all__ = ["QTensor", "fp4q_amax", "fp4q_quantize", "fp4q_quantize_fmt", "fp4q_dequant",
+           "fp4q_linear_fwd", "fp4q_linear_dgrad", "fp4q_linear_wgrad", "fp4q_linear_probe",
+           "quantize", "amax", "dequant", "ROW16", "COL16", "TILE16x16", "RNE", "SR", "F32", "BF16",
+           "UE5M3", "E4M3"]
 
 
 def _dtype_code(t: torch.Tensor) -> int:
@@ -56,15 +58,17 @@ def _ptr(t: torch.Tensor | None) -> int | None:
 class QTensor:
     """A quantized operand on the device (see fp4q_qtensor)."""
     codes: torch.Tensor      # uint8 [rows, cols/2]
-    scales: torch.Tensor     # uint8 [rows, cols/16] (ROW16) or [rows/16, cols/16] (TILE)
+    scales: torch.Tensor     # uint8 [rows, cols/B] (ROW16) or [rows/B, cols/B] (TILE), B = block
     enc_scale: torch.Tensor  # float32 [1]: the tensor scale S
     rows: int
     cols: int
     layout: int              # ROW16 or TILE16x16
+    block: int = 16          # 16, or 32 for the block-32 variant
+    scale_fmt: int = UE5M3   # UE5M3, or E4M3 (NVFP4's scale format)
 
     def c(self) -> QTensorC:
         return QTensorC(self.codes.data_ptr(), self.scales.data_ptr(), self.enc_scale.data_ptr(),
-                        self.rows, self.cols, self.layout)
+                        self.rows, self.cols, self.layout, self.block, self.scale_fmt)
 
 
 # ---------------------------------------------------------------- entry points
@@ -85,6 +89,21 @@ def fp4q_quantize(x: torch.Tensor, amax_held: torch.Tensor, target: float, layou
                              codes.data_ptr(), scales.data_ptr(), _ptr(enc_scale_out),
                              _ptr(codes_t), _ptr(scales_t), _ptr(diag), _stream())
     check("fp4q_quantize", st)
+
+
+def fp4q_quantize_fmt(x: torch.Tensor, amax_held: torch.Tensor, target: float, layout: int,
+                      block: int, scale_fmt: int, rnd: int, seed: int, subseq: int,
+                      codes: torch.Tensor, scales: torch.Tensor,
+                      enc_scale_out: torch.Tensor | None = None, codes_t: torch.Tensor | None = None,
+                      scales_t: torch.Tensor | None = None, diag: torch.Tensor | None = None) -> None:
+    _dev2d(x, "x")
+    st = lib().fp4q_quantize_fmt(x.data_ptr(), _dtype_code(x), x.shape[0], x.shape[1], _ld(x),
+                                 amax_held.data_ptr(), float(target), int(layout), int(block),
+                                 int(scale_fmt), int(rnd), int(seed) & (2 ** 64 - 1),
+                                 int(subseq) & 0xFFFFFFFF, codes.data_ptr(), scales.data_ptr(),
+                                 _ptr(enc_scale_out), _ptr(codes_t), _ptr(scales_t), _ptr(diag),
+                                 _stream())
+    check("fp4q_quantize_fmt", st)
 
 
 def fp4q_dequant(q: QTensor, out: torch.Tensor) -> None:
@@ -138,38 +157,40 @@ def amax(x: torch.Tensor) -> torch.Tensor:
 
 def quantize(x: torch.Tensor, amax_held: torch.Tensor, target: float = 448.0, layout: int = ROW16,
              rnd: int = RNE, seed: int = 0, subseq: int = 0, transposed: bool = False,
-             with_diag: bool = False):
-    """Allocate outputs and run fp4q_quantize.
+             with_diag: bool = False, block: int = 16, scale_fmt: int = UE5M3):
+    """Allocate outputs and run fp4q_quantize_fmt.
 
     Returns (q, qt, diag): q is the operand as the GEMMs read it (for COL16,
     the [cols, rows] transpose stored ROW16); with transposed=True, qt is the
     other orientation (TILE: the transposed tile copy; ROW16: the COL16
     operand [cols, rows] of the same tensor), else None; diag the int32[2]
-    repair counts or None.
+    repair counts or None. block (16 or 32) and scale_fmt (UE5M3 or E4M3)
+    select the variant.
     """
     _dev2d(x, "x")
     R, C = x.shape
+    B = block
     dev = x.device
     u8 = dict(dtype=torch.uint8, device=dev)
     S = torch.empty(1, dtype=torch.float32, device=dev)
     if layout == COL16:
         codes = torch.empty((C, R // 2), **u8)
-        scales = torch.empty((C, R // 16), **u8)
+        scales = torch.empty((C, R // B), **u8)
     else:
         codes = torch.empty((R, C // 2), **u8)
-        scales = torch.empty((R, C // 16) if layout == ROW16 else (R // 16, C // 16), **u8)
+        scales = torch.empty((R, C // B) if layout == ROW16 else (R // B, C // B), **u8)
     codes_t = scales_t = None
     if transposed:
         codes_t = torch.empty((C, R // 2), **u8)
-        scales_t = torch.empty((C // 16, R // 16) if layout == TILE16x16 else (C, R // 16), **u8)
+        scales_t = torch.empty((C // B, R // B) if layout == TILE16x16 else (C, R // B), **u8)
     diag = torch.empty(2, dtype=torch.int32, device=dev) if with_diag else None
-    fp4q_quantize(x, amax_held, target, layout, rnd, seed, subseq, codes, scales, S,
-                  codes_t, scales_t, diag)
+    fp4q_quantize_fmt(x, amax_held, target, layout, block, scale_fmt, rnd, seed, subseq, codes,
+                      scales, S, codes_t, scales_t, diag)
     if layout == COL16:
-        q = QTensor(codes, scales, S, C, R, ROW16)
+        q = QTensor(codes, scales, S, C, R, ROW16, B, scale_fmt)
     else:
-        q = QTensor(codes, scales, S, R, C, layout)
-    qt = QTensor(codes_t, scales_t, S, C, R, layout) if transposed else None
+        q = QTensor(codes, scales, S, R, C, layout, B, scale_fmt)
+    qt = QTensor(codes_t, scales_t, S, C, R, layout, B, scale_fmt) if transposed else None
     return q, qt, diag
 
 

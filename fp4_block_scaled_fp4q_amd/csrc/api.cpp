@@ -23,8 +23,10 @@ fp4q_status check_operand(const fp4q_qtensor* q) {
   if (!q) return FP4Q_E_NULL;
   if (q->rows < 0 || q->cols < 0) return FP4Q_E_SHAPE;
   if (q->layout != FP4Q_ROW16 && q->layout != FP4Q_TILE16x16) return FP4Q_E_ARG;
-  if (q->cols % 16) return FP4Q_E_SHAPE;
-  if (q->layout == FP4Q_TILE16x16 && q->rows % 16) return FP4Q_E_SHAPE;
+  if (q->block != 16 && q->block != 32) return FP4Q_E_ARG;
+  if (q->scale_fmt != FP4Q_UE5M3 && q->scale_fmt != FP4Q_E4M3) return FP4Q_E_ARG;
+  if (q->cols % q->block) return FP4Q_E_SHAPE;
+  if (q->layout == FP4Q_TILE16x16 && q->rows % q->block) return FP4Q_E_SHAPE;
   if (!q->enc_scale) return FP4Q_E_NULL;
   if (q->rows > 0 && q->cols > 0 && (!q->codes || !q->scales)) return FP4Q_E_NULL;
   if (!aligned(q->codes, 8) || !aligned(q->scales, 4)) return FP4Q_E_ALIGN;
@@ -39,6 +41,8 @@ fp4q::QOperand to_operand(const fp4q_qtensor* q) {
   o.rows = q->rows;
   o.cols = q->cols;
   o.tile = q->layout == FP4Q_TILE16x16 ? 1 : 0;
+  o.block = q->block;
+  o.scale_fmt = q->scale_fmt;
   return o;
 }
 
@@ -94,36 +98,44 @@ fp4q_status fp4q_amax(const void* x, fp4q_dtype xt, int64_t rows, int64_t cols, 
                                     static_cast<hipStream_t>(stream)));
 }
 
-fp4q_status fp4q_quantize(const void* x, fp4q_dtype xt, int64_t rows, int64_t cols, int64_t ld,
-                          const float* amax_held, float target, fp4q_layout layout,
-                          fp4q_round rnd, uint64_t seed, uint32_t subseq, uint8_t* codes,
-                          uint8_t* scales, float* enc_scale_out, uint8_t* codes_t,
-                          uint8_t* scales_t, int32_t* diag, void* stream) {
+fp4q_status fp4q_quantize_fmt(const void* x, fp4q_dtype xt, int64_t rows, int64_t cols,
+                              int64_t ld, const float* amax_held, float target, fp4q_layout layout,
+                              int32_t block, fp4q_scale_fmt scale_fmt, fp4q_round rnd,
+                              uint64_t seed, uint32_t subseq, uint8_t* codes, uint8_t* scales,
+                              float* enc_scale_out, uint8_t* codes_t, uint8_t* scales_t,
+                              int32_t* diag, void* stream) {
   const int es = elem_size(xt);
   if (!es) return FP4Q_E_DTYPE;
   if (layout != FP4Q_ROW16 && layout != FP4Q_COL16 && layout != FP4Q_TILE16x16) return FP4Q_E_ARG;
+  if (block != 16 && block != 32) return FP4Q_E_ARG;
+  if (scale_fmt != FP4Q_UE5M3 && scale_fmt != FP4Q_E4M3) return FP4Q_E_ARG;
   if (rnd != FP4Q_RNE && rnd != FP4Q_SR) return FP4Q_E_ARG;
   if (!(target > 0.0f) || !std::isfinite(target)) return FP4Q_E_ARG;
   if ((codes_t == nullptr) != (scales_t == nullptr)) return FP4Q_E_ARG;
   if (codes_t && layout == FP4Q_COL16) return FP4Q_E_ARG;
-  // ROW16 with the second orientation also needs whole column blocks
-  if (codes_t && layout == FP4Q_ROW16 && rows % 16) return FP4Q_E_SHAPE;
+  // ROW with the second orientation also needs whole column blocks
+  if (codes_t && layout == FP4Q_ROW16 && rows % block) return FP4Q_E_SHAPE;
   if (!amax_held) return FP4Q_E_NULL;
   if (rows < 0 || cols < 0 || ld < cols) return FP4Q_E_SHAPE;
-  if (layout != FP4Q_COL16 && cols % 16) return FP4Q_E_SHAPE;
-  if (layout != FP4Q_ROW16 && rows % 16) return FP4Q_E_SHAPE;
+  if (layout != FP4Q_COL16 && cols % block) return FP4Q_E_SHAPE;
+  if (layout != FP4Q_ROW16 && rows % block) return FP4Q_E_SHAPE;
   if (layout == FP4Q_COL16 && cols % 8) return FP4Q_E_ALIGN;
   const bool nonempty = rows > 0 && cols > 0;
   if (nonempty) {
     if (!x || !codes || !scales) return FP4Q_E_NULL;
     if (!aligned(x, 16) || (ld * es) % 16) return FP4Q_E_ALIGN;
     if (!aligned(codes, 8) || (codes_t && !aligned(codes_t, 8))) return FP4Q_E_ALIGN;
+    // workgroup counts of the kernels (see the launchers)
+    int64_t groups;
     if (layout == FP4Q_ROW16 && !codes_t) {
-      const int64_t segs = (cols / 16 + 63) / 64;
-      if (rows * segs > kMaxGridX) return FP4Q_E_SHAPE;
-    } else if (((cols + 63) / 64) * ((rows + 63) / 64) > kMaxGridX) {
-      return FP4Q_E_SHAPE;
+      groups = rows * ((cols / block + 63) / 64);
+    } else if (layout == FP4Q_TILE16x16) {
+      groups = ((cols / 8 + 255) / 256) * (rows / 16);
+    } else {
+      const int64_t tc = 1024 / block, tr = 4 * block;
+      groups = ((cols + tc - 1) / tc) * ((rows + tr - 1) / tr);
     }
+    if (groups > kMaxGridX) return FP4Q_E_SHAPE;
   }
   if ((enc_scale_out && !aligned(enc_scale_out, 4)) || (diag && !aligned(diag, 4)))
     return FP4Q_E_ALIGN;
@@ -136,6 +148,8 @@ fp4q_status fp4q_quantize(const void* x, fp4q_dtype xt, int64_t rows, int64_t co
   a.amax_held = amax_held;
   a.target = target;
   a.layout = (int)layout;
+  a.block = block;
+  a.scale_fmt = (int)scale_fmt;
   a.sr = rnd == FP4Q_SR ? 1 : 0;
   a.seed = seed;
   a.subseq = subseq;
@@ -146,6 +160,16 @@ fp4q_status fp4q_quantize(const void* x, fp4q_dtype xt, int64_t rows, int64_t co
   a.scales_t = scales_t;
   a.diag = diag;
   return from_hip(fp4q::launch_quantize(a, static_cast<hipStream_t>(stream)));
+}
+
+fp4q_status fp4q_quantize(const void* x, fp4q_dtype xt, int64_t rows, int64_t cols, int64_t ld,
+                          const float* amax_held, float target, fp4q_layout layout,
+                          fp4q_round rnd, uint64_t seed, uint32_t subseq, uint8_t* codes,
+                          uint8_t* scales, float* enc_scale_out, uint8_t* codes_t,
+                          uint8_t* scales_t, int32_t* diag, void* stream) {
+  return fp4q_quantize_fmt(x, xt, rows, cols, ld, amax_held, target, layout, 16, FP4Q_UE5M3, rnd,
+                           seed, subseq, codes, scales, enc_scale_out, codes_t, scales_t, diag,
+                           stream);
 }
 
 fp4q_status fp4q_dequant(const fp4q_qtensor* q, void* out, fp4q_dtype ot, void* stream) {

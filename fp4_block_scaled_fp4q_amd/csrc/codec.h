@@ -79,7 +79,7 @@ __device__ __forceinline__ uint32_t ue5m3_encode(float raw, uint32_t* flags) {
 // product.
 __device__ __forceinline__ float div6_rn(float a) { return (float)((double)a * (1.0 / 6.0)); }
 
-// RN(s / d) for s > 0 and d a positive UE5M3 value, as RN32(s * 1/d) in
+// RN(s / d) for s > 0 and d a positive UE5M3 or E4M3 value, as RN32(s * 1/d) in
 // double with a Newton-refined reciprocal. d = (8 + m) 2^k with an odd part
 // of 8 + m in {1, 3, 5, ..., 15}: the quotient is either exact or at least
 // 2^-29 (relative) away from every binary32 midpoint, again far more than
@@ -91,20 +91,41 @@ __device__ __forceinline__ float div_rn(double s, float d) {
   return (float)(s * y);
 }
 
+// E4M3 block scale (NVFP4's format; codes 0x00..0x7E, 448 the largest, 2^-9
+// the smallest subnormal): its codebook is the UE5M3 codebook times 2^8, cut
+// at 448. So the nearest E4M3 code of raw is the nearest UE5M3 code of
+// raw * 2^-8 (an exact scaling wherever the result can be non-zero), with
+// saturation once raw > 464 (the midpoint to the next point, 480; 464 itself
+// ties to the even code 0x7E); zero-rounding repairs to 0x01 as for UE5M3.
+__device__ __forceinline__ uint32_t e4m3_encode(float raw, uint32_t* flags) {
+  const float q = raw * 0.00390625f;
+  uint32_t f;
+  const uint32_t code = ue5m3_encode(q, &f);
+  const bool sat = f2u(q) > 0x3FE80000u;  // q > 1.8125, i.e. raw > 464
+  *flags = (f & 1u) | (sat ? 2u : 0u);
+  return sat ? 0x7Eu : code;
+}
+
+// Value of a scale code: UE5M3, or E4M3 (UE5M3 value times 256).
+__device__ __forceinline__ float scale_value(uint32_t code, bool e4m3) {
+  return ue5m3_value(code) * (e4m3 ? 256.0f : 1.0f);
+}
+
 // Per-block quantities shared by every element of a block.
 struct BlockScale {
-  uint32_t code;  // UE5M3 code written to the scale array (0 for an all-zero block)
+  uint32_t code;  // scale code written to the scale array (0 for an all-zero block)
   float mul;      // r = RN(S / dec); 0 for an all-zero block, so x * r keeps only the sign
   uint32_t flags; // repair flags
 };
 
-// bamax is the block's max |x| as a sign-cleared bit pattern.
-__device__ __forceinline__ BlockScale block_scale(uint32_t bamax, float S, double S_d) {
+// bamax is the block's max |x| as a sign-cleared bit pattern; e4m3 selects
+// the scale format (uniform across a launch).
+__device__ __forceinline__ BlockScale block_scale(uint32_t bamax, float S, double S_d, bool e4m3) {
   const float d6 = div6_rn(u2f(bamax));
   const float raw = d6 * S;
   uint32_t flags;
-  const uint32_t code = ue5m3_encode(raw, &flags);
-  const float mul = div_rn(S_d, ue5m3_value(code));
+  const uint32_t code = e4m3 ? e4m3_encode(raw, &flags) : ue5m3_encode(raw, &flags);
+  const float mul = div_rn(S_d, scale_value(code, e4m3));
   BlockScale b;
   const bool nz = bamax != 0u;
   b.code = nz ? code : 0u;

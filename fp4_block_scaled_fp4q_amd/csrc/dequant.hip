@@ -26,15 +26,16 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict_
                                                       const uint8_t* __restrict__ scales,
                                                       const float* __restrict__ enc_scale,
                                                       int64_t rows, int64_t cols, int tile,
-                                                      void* __restrict__ out, int out_es) {
+                                                      int block, int e4m3, void* __restrict__ out,
+                                                      int out_es) {
   const int64_t words_per_row = cols / 8;
   const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (g >= rows * words_per_row) return;
   const int64_t r = g / words_per_row;
   const int64_t w = g - r * words_per_row;
   const uint32_t d = reinterpret_cast<const uint32_t*>(codes + r * (cols / 2))[w];
-  const int64_t srow = tile ? (r >> 4) : r;
-  const float dec = ue5m3_value(scales[srow * (cols / 16) + (w >> 1)]);
+  const int64_t srow = tile ? r / block : r;
+  const float dec = scale_value(scales[srow * (cols / block) + (w * 8) / block], e4m3 != 0);
   const float S = *enc_scale;
   float v[8];
 #pragma unroll
@@ -57,7 +58,7 @@ hipError_t launch_dequant(const QOperand& q, void* out, int out_es, hipStream_t 
   const int64_t n = q.rows * (q.cols / 8);
   if (n == 0) return hipSuccess;
   hipLaunchKernelGGL(dequant_kernel, dim3((uint32_t)((n + 255) / 256)), dim3(256), 0, s, q.codes,
-                     q.scales, q.enc_scale, q.rows, q.cols, q.tile, out, out_es);
+                     q.scales, q.enc_scale, q.rows, q.cols, q.tile, q.block, q.scale_fmt, out, out_es);
   return hipGetLastError();
 }
 

@@ -60,29 +60,47 @@ struct RowSeg {
   uint32_t s;      // 4 scale bytes, block j in bits 8j+7:8j
 };
 
+// Scale bytes of the four 16-element blocks of a 64-element segment: one
+// byte each for blocks of 16; for blocks of 32 each of the segment's two
+// scale bytes is repeated for its two halves, so consumers index by block
+// of 16 either way.
+__device__ __forceinline__ uint32_t widen32(uint32_t two) {
+  const uint32_t lo = two & 0xFFu, hi = (two >> 8) & 0xFFu;
+  return lo | (lo << 8) | (hi << 16) | (hi << 24);
+}
+
 // K % 64 == 0: a whole segment is in bounds; rows past the end are clamped
 // to the last row (their products only reach outputs that are not stored),
-// so the load is branch-free.
+// so the load is branch-free. blk32: blocks of 32 (else 16).
 __device__ __forceinline__ RowSeg load_seg_full(const uint8_t* __restrict__ codes,
                                                 const uint8_t* __restrict__ scales, int64_t rows,
-                                                int64_t K, int tile_shift, int64_t r, int64_t k0) {
+                                                int64_t K, int tile_shift, bool blk32, int64_t r,
+                                                int64_t k0) {
   r = r < rows ? r : rows - 1;
   const uint8_t* cp = codes + r * (K / 2) + k0 / 2;
-  const uint8_t* sp = scales + (r >> tile_shift) * (K / 16) + k0 / 16;
   RowSeg g;
   g.c0 = *reinterpret_cast<const uint4*>(cp);
   g.c1 = *reinterpret_cast<const uint4*>(cp + 16);
-  g.s = *reinterpret_cast<const uint32_t*>(sp);
+  if (blk32) {
+    const uint8_t* sp = scales + (r >> tile_shift) * (K / 32) + k0 / 32;
+    g.s = widen32(*reinterpret_cast<const uint16_t*>(sp));
+  } else {
+    const uint8_t* sp = scales + (r >> tile_shift) * (K / 16) + k0 / 16;
+    g.s = *reinterpret_cast<const uint32_t*>(sp);
+  }
   return g;
 }
 
-// General K (a multiple of 16): blocks at or beyond K read as zero codes.
+// General K (a multiple of the block size): blocks at or beyond K read as
+// zero codes.
 __device__ __forceinline__ RowSeg load_seg_tail(const uint8_t* __restrict__ codes,
                                                 const uint8_t* __restrict__ scales, int64_t rows,
-                                                int64_t K, int tile_shift, int64_t r, int64_t k0) {
+                                                int64_t K, int tile_shift, bool blk32, int64_t r,
+                                                int64_t k0) {
   r = r < rows ? r : rows - 1;
+  const int bl = blk32 ? 32 : 16;
   const uint8_t* cp = codes + r * (K / 2);
-  const uint8_t* sp = scales + (r >> tile_shift) * (K / 16);
+  const uint8_t* sp = scales + (r >> tile_shift) * (K / bl);
   uint2 b[4];
   uint32_t s = 0u;
 #pragma unroll
@@ -90,7 +108,7 @@ __device__ __forceinline__ RowSeg load_seg_tail(const uint8_t* __restrict__ code
     const int64_t kb = k0 + 16 * j;
     if (kb < K) {
       b[j] = *reinterpret_cast<const uint2*>(cp + kb / 2);
-      s |= (uint32_t)sp[kb / 16] << (8 * j);
+      s |= (uint32_t)sp[kb / bl] << (8 * j);
     } else {
       b[j] = make_uint2(0u, 0u);
     }
@@ -105,9 +123,10 @@ __device__ __forceinline__ RowSeg load_seg_tail(const uint8_t* __restrict__ code
 template <bool kFullK>
 __device__ __forceinline__ RowSeg load_seg(const uint8_t* __restrict__ codes,
                                            const uint8_t* __restrict__ scales, int64_t rows,
-                                           int64_t K, int tile_shift, int64_t r, int64_t k0) {
-  return kFullK ? load_seg_full(codes, scales, rows, K, tile_shift, r, k0)
-                : load_seg_tail(codes, scales, rows, K, tile_shift, r, k0);
+                                           int64_t K, int tile_shift, bool blk32, int64_t r,
+                                           int64_t k0) {
+  return kFullK ? load_seg_full(codes, scales, rows, K, tile_shift, blk32, r, k0)
+                : load_seg_tail(codes, scales, rows, K, tile_shift, blk32, r, k0);
 }
 
 // 8 codes (one 32-bit word, element e in bits 4e+3:4e) of a block with
@@ -162,7 +181,9 @@ __global__ __launch_bounds__(64 * kWavesM * kWavesN) void gemm_kernel(
     const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales, int a_shift,
     const float* __restrict__ a_S, const uint8_t* __restrict__ b_codes,
     const uint8_t* __restrict__ b_scales, int b_shift, const float* __restrict__ b_S, int64_t M,
-    int64_t N, int64_t K, int tiles_m, int tiles_n, int snap_log2, void* __restrict__ y) {
+    int64_t N, int64_t K, int tiles_m, int tiles_n, int snap_log2, int fmt, void* __restrict__ y) {
+  // fmt bits: 0 A blocks of 32, 1 A E4M3 scales, 2 B blocks of 32, 3 B E4M3 scales
+  const bool a_blk32 = fmt & 1, a_e4m3 = fmt & 2, b_blk32 = fmt & 4, b_e4m3 = fmt & 8;
   constexpr int kT = 64 * kWavesM * kWavesN;  // threads
   constexpr int kTM = kBM / kWavesM;           // wave tile rows
   constexpr int kTN = kBN / kWavesN;           // wave tile cols
@@ -208,8 +229,8 @@ __global__ __launch_bounds__(64 * kWavesM * kWavesN) void gemm_kernel(
 #pragma unroll
     for (int i = 0; i < kRows; ++i) {
       const int q = tid + i * kT;
-      g[i] = q < kBM ? load_seg<kFullK>(a_codes, a_scales, M, K, a_shift, m0 + q, k0)
-                    : load_seg<kFullK>(b_codes, b_scales, N, K, b_shift, n0 + (q - kBM), k0);
+      g[i] = q < kBM ? load_seg<kFullK>(a_codes, a_scales, M, K, a_shift, a_blk32, m0 + q, k0)
+                    : load_seg<kFullK>(b_codes, b_scales, N, K, b_shift, b_blk32, n0 + (q - kBM), k0);
     }
   };
   // one decode8 piece p (0 .. kPieces-1) of block s into buffer `buf`
@@ -217,7 +238,7 @@ __global__ __launch_bounds__(64 * kWavesM * kWavesN) void gemm_kernel(
     const int i = p >> 1;
     const int q = tid + i * kT;
     const int c = 2 * s + (p & 1);
-    const float dec = ue5m3_value((g[i].s >> (8 * s)) & 0xFFu);
+    const float dec = scale_value((g[i].s >> (8 * s)) & 0xFFu, q < kBM ? a_e4m3 : b_e4m3);
     buf[slot<kSwz>(q, c)] = decode8(seg_word(g[i], c), dec);
   };
 
@@ -412,10 +433,14 @@ hipError_t launch_tiled(const QOperand& a, const QOperand& b, void* y, int y_es,
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);
   if (e != hipSuccess) return e;
   const dim3 grid((uint32_t)(tiles_m * tiles_n)), block(64 * kWM * kWN);
+  const int a_shift = a.tile ? (a.block == 32 ? 5 : 4) : 0;
+  const int b_shift = b.tile ? (b.block == 32 ? 5 : 4) : 0;
+  const int fmt = (a.block == 32 ? 1 : 0) | (a.scale_fmt ? 2 : 0) | (b.block == 32 ? 4 : 0) |
+                  (b.scale_fmt ? 8 : 0);
 #define FP4Q_GEMM(FK, F32)                                                                     \
   hipLaunchKernelGGL((gemm_kernel<kBM, kBN, FK, F32, kWM, kWN, kSW, kProbe>), grid, block,      \
-                     lds_bytes, s, a.codes, a.scales, a.tile ? 4 : 0, a.enc_scale, b.codes,      \
-                     b.scales, b.tile ? 4 : 0, b.enc_scale, M, N, K, tiles_m, tiles_n, snap_log2, y)
+                     lds_bytes, s, a.codes, a.scales, a_shift, a.enc_scale, b.codes, b.scales,    \
+                     b_shift, b.enc_scale, M, N, K, tiles_m, tiles_n, snap_log2, fmt, y)
   if (full_k) {
     if (y_es == 4) FP4Q_GEMM(true, true);
     else FP4Q_GEMM(true, false);

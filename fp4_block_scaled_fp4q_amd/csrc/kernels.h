@@ -18,7 +18,9 @@ struct QuantArgs {
   int64_t rows, cols, ld;
   const float* amax_held;
   float target;
-  int layout;  // 0 ROW16, 1 COL16, 2 TILE16x16
+  int layout;  // 0 ROW16, 1 COL16, 2 TILE16x16 (blocks along a row, down a column, square)
+  int block;   // 16 or 32
+  int scale_fmt;  // 0 UE5M3, 1 E4M3
   int sr;      // 0 RNE, 1 SR
   uint64_t seed;
   uint32_t subseq;
@@ -36,7 +38,9 @@ struct QOperand {
   const uint8_t* scales;
   const float* enc_scale;
   int64_t rows, cols;
-  int tile;  // 0: ROW16 scales [rows][cols/16]; 1: TILE16x16 scales [rows/16][cols/16]
+  int tile;  // 0: ROW16 scales [rows][cols/block]; 1: TILE16x16 scales [rows/block][cols/block]
+  int block;      // 16 or 32
+  int scale_fmt;  // 0 UE5M3, 1 E4M3 (value = UE5M3 value * 256)
 };
 
 hipError_t launch_dequant(const QOperand& q, void* out, int out_es, hipStream_t s);

@@ -14,6 +14,11 @@
 // ROW16 may also emit the COL16 outputs of the same tensor in the same pass
 // (one read of the input, one Philox word per element for both).
 //
+// Variants: blocks of 32 instead of 16 (the page's block-32 run, §7.3; the
+// shapes above with 32 in place of 16, and 32 x 32 weight tiles) and E4M3
+// block scales instead of UE5M3 (NVFP4's scale format, §3), selected per
+// call.
+//
 // The RNE kernels are HBM-bound: every input byte is read once with 128-bit
 // loads and the per-element work is a widening, one multiply and half a
 // hardware FP4 conversion. SR adds a Philox4x32-10 evaluation per four
@@ -139,43 +144,57 @@ __device__ __forceinline__ int xcd_order(int L, int n) {
   return xcd < full ? xcd * per + local : full * per + (xcd - full) * (per - 1) + local;
 }
 
-// ------------------------------------------------------------------ ROW16
-// One 16-element block per lane (two Octs). A workgroup (one wave) covers
-// kRowThreads consecutive blocks of one row; small workgroups measured
-// fastest for this stream.
+// ------------------------------------------------------------------ ROW
+// One block (kBlk = 16 or 32 elements, kBlk / 8 Octs) per lane. A workgroup
+// (one wave) covers kRowThreads consecutive blocks of one row; small
+// workgroups measured fastest for this stream.
 constexpr int kRowThreads = 64;
 
-template <bool kBF16, bool kSR>
-__global__ __launch_bounds__(kRowThreads) void quant_row16_kernel(
+// Stores the kBlk / 2 code bytes of one block (8-byte aligned destination).
+template <int kBlk>
+__device__ __forceinline__ void store_block_codes(uint8_t* dst, const uint32_t (&cw)[kBlk / 8]) {
+#pragma clang loop unroll(full)
+  for (int j = 0; j < kBlk / 16; ++j)
+    reinterpret_cast<uint2*>(dst)[j] = make_uint2(cw[2 * j], cw[2 * j + 1]);
+}
+
+template <bool kBF16, bool kSR, int kBlk>
+__global__ __launch_bounds__(kRowThreads) void quant_row_kernel(
     const uint8_t* __restrict__ x, int64_t cols, int64_t ld_bytes, int segs_per_row,
-    const float* __restrict__ amax_held, float target, uint64_t seed, uint32_t subseq,
+    const float* __restrict__ amax_held, float target, int e4m3, uint64_t seed, uint32_t subseq,
     uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, float* __restrict__ enc_out,
     int32_t* __restrict__ diag) {
   constexpr int es = kBF16 ? 2 : 4;
+  constexpr int kOcts = kBlk / 8;
   const int64_t row = blockIdx.x / segs_per_row;
   const int seg = blockIdx.x - (int)(row * segs_per_row);
   const float S = tensor_scale(*amax_held, target);
   const double S_d = (double)S;
   if (enc_out && blockIdx.x == 0 && threadIdx.x == 0) *enc_out = S;
-  const int64_t nblk = cols / 16;
+  const int64_t nblk = cols / kBlk;
   const int64_t blk = (int64_t)seg * kRowThreads + threadIdx.x;
   uint32_t nzero = 0u, nsat = 0u;
   if (blk < nblk) {
-    const uint8_t* p = x + row * ld_bytes + blk * 16 * es;
-    Oct<kBF16> a, b;
-    a.load(p);
-    b.load(p + 8 * es);
-    const BlockScale s = block_scale(max(a.absmax(), b.absmax()), S, S_d);
-    uint32_t w[16];
+    const uint8_t* p = x + row * ld_bytes + blk * kBlk * es;
+    Oct<kBF16> o[kOcts];
+    uint32_t m = 0u;
+#pragma clang loop unroll(full)
+    for (int j = 0; j < kOcts; ++j) {
+      o[j].load(p + 8 * j * es);
+      m = max(m, o[j].absmax());
+    }
+    const BlockScale s = block_scale(m, S, S_d, e4m3 != 0);
+    uint32_t w[kBlk];
     if (kSR) {
-      const uint64_t idx0 = (uint64_t)row * (uint64_t)cols + (uint64_t)blk * 16;
-      words8(idx0, seed, subseq, w);
-      words8(idx0 + 8, seed, subseq, w + 8);
+      const uint64_t idx0 = (uint64_t)row * (uint64_t)cols + (uint64_t)blk * kBlk;
+#pragma clang loop unroll(full)
+      for (int j = 0; j < kOcts; ++j) words8(idx0 + 8 * j, seed, subseq, w + 8 * j);
     }
     const bool mi = __builtin_isinf(s.mul);
-    const uint32_t lo = encode_oct<kBF16, kSR>(a, s.mul, mi, w);
-    const uint32_t hi = encode_oct<kBF16, kSR>(b, s.mul, mi, w + 8);
-    *reinterpret_cast<uint2*>(codes + row * (cols / 2) + blk * 8) = make_uint2(lo, hi);
+    uint32_t cw[kOcts];
+#pragma clang loop unroll(full)
+    for (int j = 0; j < kOcts; ++j) cw[j] = encode_oct<kBF16, kSR>(o[j], s.mul, mi, w + 8 * j);
+    store_block_codes<kBlk>(codes + row * (cols / 2) + blk * (kBlk / 2), cw);
     scales[row * nblk + blk] = (uint8_t)s.code;
     nzero = s.flags & 1u;
     nsat = s.flags >> 1;
@@ -183,36 +202,57 @@ __global__ __launch_bounds__(kRowThreads) void quant_row16_kernel(
   if (diag) add_diag(diag, nzero, nsat);
 }
 
-// ------------------------------------------------------------------ ROW16 + COL16
-// A workgroup owns a 64 x 64 tile. Phase 1: thread t takes row t / 4 and 16
-// columns 16 (t % 4) .. +15 (one ROW16 block): coalesced loads, the ROW16
-// codes and scale when requested, and for SR the 16 Philox words; it parks
-// the raw inputs (and words) in LDS. Phase 2: thread t takes column t % 64
-// and rows 16 (t / 64) .. +15 (one COL16 block), reading LDS down the column
-// (a wave reads one LDS row, 64 consecutive elements: no bank conflicts),
-// and writes the COL16 codes and scale. Each element's Philox word serves
-// both orientations. Tiles are ordered so that one XCD runs the row tiles of
-// a column tile back to back (they fill the same lines of the COL16 codes).
-constexpr int kTT = 64;  // tile rows and columns
+// ------------------------------------------------------------------ ROW + COL
+// A workgroup owns a tile of kDualRows(kBlk) = 4 kBlk rows by kDualCols(kBlk)
+// = 1024 / kBlk columns (64 x 64 for blocks of 16, 128 x 32 for 32), with
+// one block per thread in each phase. Phase 1: thread t takes one row block
+// (row t / (cols per tile / kBlk)): coalesced loads, the ROW codes and scale
+// when requested, and for SR the Philox words; it parks the raw inputs (and
+// words) in LDS. Phase 2: thread t takes column t % cols-per-tile and the
+// kBlk rows of block t / cols-per-tile (one COL block), reading LDS down the
+// column, and writes the COL codes and scale. Each element's Philox word
+// serves both orientations. Tiles are ordered so that one XCD runs the row
+// tiles of a column tile back to back (they fill the same lines of the COL
+// codes).
+template <int kBlk>
+constexpr int kDualCols() { return 1024 / kBlk; }
+template <int kBlk>
+constexpr int kDualRows() { return 4 * kBlk; }
+template <int kBlk>
+constexpr int kDualThreads() { return 4 * kDualCols<kBlk>(); }
 
-template <bool kBF16, bool kSR, bool kRow>
-__global__ __launch_bounds__(kThreads) void quant_dual_kernel(
+// 8 RNE codes of v[0..7] * mu (the conversion takes a constant selector).
+__device__ __forceinline__ uint32_t rne8(const float* v, float mu) {
+  uint32_t w = 0u;
+  w = FP4Q_ENC2(w, v[0] * mu, v[1] * mu, 0);
+  w = FP4Q_ENC2(w, v[2] * mu, v[3] * mu, 1);
+  w = FP4Q_ENC2(w, v[4] * mu, v[5] * mu, 2);
+  w = FP4Q_ENC2(w, v[6] * mu, v[7] * mu, 3);
+  return w;
+}
+
+template <bool kBF16, bool kSR, bool kRow, int kBlk>
+__global__ __launch_bounds__(kDualThreads<kBlk>()) void quant_dual_kernel(
     const uint8_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld_bytes, int col_tiles,
-    int row_tiles, const float* __restrict__ amax_held, float target, uint64_t seed,
+    int row_tiles, const float* __restrict__ amax_held, float target, int e4m3, uint64_t seed,
     uint32_t subseq, uint8_t* __restrict__ codes_r, uint8_t* __restrict__ scales_r,
     uint8_t* __restrict__ codes_c, uint8_t* __restrict__ scales_c, float* __restrict__ enc_out,
     int32_t* __restrict__ diag) {
   constexpr int es = kBF16 ? 2 : 4;
-  constexpr int kXPitch = kTT * es + 16;  // bytes per LDS row of inputs (16 B pad)
-  constexpr int kWPitch = kTT * 4 + 16;   // bytes per LDS row of Philox words
-  __shared__ __attribute__((aligned(16))) uint8_t lx[kTT * kXPitch];
-  __shared__ __attribute__((aligned(16))) uint8_t lw[kSR ? kTT * kWPitch : 16];
+  constexpr int kTC = kDualCols<kBlk>();
+  constexpr int kTR = kDualRows<kBlk>();
+  constexpr int kOcts = kBlk / 8;
+  constexpr int kBPR = kTC / kBlk;          // row blocks per tile row
+  constexpr int kXPitch = kTC * es + 16;    // bytes per LDS row of inputs (16 B pad)
+  constexpr int kWPitch = kTC * 4 + 16;     // bytes per LDS row of Philox words
+  __shared__ __attribute__((aligned(16))) uint8_t lx[kTR * kXPitch];
+  __shared__ __attribute__((aligned(16))) uint8_t lw[kSR ? kTR * kWPitch : 16];
 
   const int item = xcd_order(blockIdx.x, col_tiles * row_tiles);
   const int ct = item / row_tiles;
   const int rt = item - ct * row_tiles;
-  const int64_t r0 = (int64_t)rt * kTT;
-  const int64_t c0 = (int64_t)ct * kTT;
+  const int64_t r0 = (int64_t)rt * kTR;
+  const int64_t c0 = (int64_t)ct * kTC;
   const float S = tensor_scale(*amax_held, target);
   const double S_d = (double)S;
   if (enc_out && blockIdx.x == 0 && threadIdx.x == 0) *enc_out = S;
@@ -221,91 +261,91 @@ __global__ __launch_bounds__(kThreads) void quant_dual_kernel(
 
   // ---- phase 1: one row block per thread
   {
-    const int r = t >> 2;
-    const int q = t & 3;
+    const int r = t / kBPR;
+    const int q = t % kBPR;
     const int64_t gr = r0 + r;
-    const int64_t gc = c0 + 16 * q;
+    const int64_t gc = c0 + kBlk * q;
     const bool vr = gr < rows;
-    const bool v0 = vr && gc < cols;
-    const bool v1 = vr && gc + 8 < cols;
-    Oct<kBF16> a, b;
-    if (v0) a.load(x + gr * ld_bytes + gc * es); else a.zero();
-    if (v1) b.load(x + gr * ld_bytes + (gc + 8) * es); else b.zero();
-    uint32_t w[16];
+    Oct<kBF16> o[kOcts];
+#pragma clang loop unroll(full)
+    for (int j = 0; j < kOcts; ++j) {
+      if (vr && gc + 8 * j < cols) o[j].load(x + gr * ld_bytes + (gc + 8 * j) * es);
+      else o[j].zero();
+    }
+    uint32_t w[kBlk];
     if (kSR) {
       const uint64_t idx0 = (uint64_t)gr * (uint64_t)cols + (uint64_t)gc;
-      words8(idx0, seed, subseq, w);
-      words8(idx0 + 8, seed, subseq, w + 8);
+#pragma clang loop unroll(full)
+      for (int j = 0; j < kOcts; ++j) words8(idx0 + 8 * j, seed, subseq, w + 8 * j);
     }
-    if (kRow && v0) {  // cols % 16 == 0 here, so v0 implies v1
-      const BlockScale s = block_scale(max(a.absmax(), b.absmax()), S, S_d);
+    if (kRow && vr && gc < cols) {  // cols % kBlk == 0 here: the whole block is valid
+      uint32_t m = 0u;
+#pragma clang loop unroll(full)
+      for (int j = 0; j < kOcts; ++j) m = max(m, o[j].absmax());
+      const BlockScale s = block_scale(m, S, S_d, e4m3 != 0);
       const bool mi = __builtin_isinf(s.mul);
-      const uint32_t lo = encode_oct<kBF16, kSR>(a, s.mul, mi, w);
-      const uint32_t hi = encode_oct<kBF16, kSR>(b, s.mul, mi, w + 8);
-      *reinterpret_cast<uint2*>(codes_r + gr * (cols / 2) + gc / 2) = make_uint2(lo, hi);
-      scales_r[gr * (cols / 16) + gc / 16] = (uint8_t)s.code;
+      uint32_t cw[kOcts];
+#pragma clang loop unroll(full)
+      for (int j = 0; j < kOcts; ++j) cw[j] = encode_oct<kBF16, kSR>(o[j], s.mul, mi, w + 8 * j);
+      store_block_codes<kBlk>(codes_r + gr * (cols / 2) + gc / 2, cw);
+      scales_r[gr * (cols / kBlk) + gc / kBlk] = (uint8_t)s.code;
       nzero += s.flags & 1u;
       nsat += s.flags >> 1;
     }
-    uint4* dx = reinterpret_cast<uint4*>(lx + r * kXPitch + 16 * q * es);
-    if (kBF16) {
-      dx[0] = make_uint4(a.d[0], a.d[1], a.d[2], a.d[3]);
-      dx[1] = make_uint4(b.d[0], b.d[1], b.d[2], b.d[3]);
-    } else {
-      dx[0] = make_uint4(a.d[0], a.d[1], a.d[2], a.d[3]);
-      dx[1] = make_uint4(a.d[4], a.d[5], a.d[6], a.d[7]);
-      dx[2] = make_uint4(b.d[0], b.d[1], b.d[2], b.d[3]);
-      dx[3] = make_uint4(b.d[4], b.d[5], b.d[6], b.d[7]);
+    uint4* dx = reinterpret_cast<uint4*>(lx + r * kXPitch + kBlk * q * es);
+#pragma clang loop unroll(full)
+    for (int j = 0; j < kOcts; ++j) {
+      if (kBF16) {
+        dx[j] = make_uint4(o[j].d[0], o[j].d[1], o[j].d[2], o[j].d[3]);
+      } else {
+        dx[2 * j] = make_uint4(o[j].d[0], o[j].d[1], o[j].d[2], o[j].d[3]);
+        dx[2 * j + 1] = make_uint4(o[j].d[4], o[j].d[5], o[j].d[6], o[j].d[7]);
+      }
     }
     if (kSR) {
-      uint4* dw = reinterpret_cast<uint4*>(lw + r * kWPitch + 64 * q);
+      uint4* dw = reinterpret_cast<uint4*>(lw + r * kWPitch + 4 * kBlk * q);
 #pragma clang loop unroll(full)
-      for (int k = 0; k < 4; ++k) dw[k] = make_uint4(w[4 * k], w[4 * k + 1], w[4 * k + 2], w[4 * k + 3]);
+      for (int k = 0; k < kBlk / 4; ++k) dw[k] = make_uint4(w[4 * k], w[4 * k + 1], w[4 * k + 2], w[4 * k + 3]);
     }
   }
   __syncthreads();
 
   // ---- phase 2: one column block per thread
   {
-    const int c = t & (kTT - 1);
-    const int rb = t >> 6;
+    const int c = t % kTC;
+    const int rb = t / kTC;
     const int64_t gc = c0 + c;
-    const int64_t gr0 = r0 + 16 * rb;
+    const int64_t gr0 = r0 + kBlk * rb;
     if (gc < cols && gr0 < rows) {
-      float v[16];
+      float v[kBlk];
       uint32_t m = 0u;
 #pragma clang loop unroll(full)
-      for (int r = 0; r < 16; ++r) {
-        const uint8_t* src = lx + (16 * rb + r) * kXPitch + c * es;
+      for (int r = 0; r < kBlk; ++r) {
+        const uint8_t* src = lx + (kBlk * rb + r) * kXPitch + c * es;
         v[r] = kBF16 ? u2f((uint32_t)*reinterpret_cast<const uint16_t*>(src) << 16)
                      : *reinterpret_cast<const float*>(src);
         m = max(m, f2u(v[r]) & 0x7FFFFFFFu);
       }
-      const BlockScale s = block_scale(m, S, S_d);
+      const BlockScale s = block_scale(m, S, S_d, e4m3 != 0);
       const bool mi = __builtin_isinf(s.mul);
-      uint32_t cw[2] = {0u, 0u};
+      uint32_t cw[kOcts];
+#pragma clang loop unroll(full)
+      for (int j = 0; j < kOcts; ++j) cw[j] = 0u;
       if (__builtin_expect(mi, 0)) {
 #pragma clang loop unroll(full)
-        for (int r = 0; r < 16; ++r) cw[r >> 3] |= inf_code(v[r]) << (4 * (r & 7));
+        for (int r = 0; r < kBlk; ++r) cw[r >> 3] |= inf_code(v[r]) << (4 * (r & 7));
       } else if (kSR) {
 #pragma clang loop unroll(full)
-        for (int r = 0; r < 16; ++r) {
-          const uint32_t wr = *reinterpret_cast<const uint32_t*>(lw + (16 * rb + r) * kWPitch + 4 * c);
+        for (int r = 0; r < kBlk; ++r) {
+          const uint32_t wr = *reinterpret_cast<const uint32_t*>(lw + (kBlk * rb + r) * kWPitch + 4 * c);
           cw[r >> 3] |= sr_code(v[r] * s.mul, wr) << (4 * (r & 7));
         }
       } else {
-        const float mu = s.mul;
-        cw[0] = FP4Q_ENC2(cw[0], v[0] * mu, v[1] * mu, 0);
-        cw[0] = FP4Q_ENC2(cw[0], v[2] * mu, v[3] * mu, 1);
-        cw[0] = FP4Q_ENC2(cw[0], v[4] * mu, v[5] * mu, 2);
-        cw[0] = FP4Q_ENC2(cw[0], v[6] * mu, v[7] * mu, 3);
-        cw[1] = FP4Q_ENC2(cw[1], v[8] * mu, v[9] * mu, 0);
-        cw[1] = FP4Q_ENC2(cw[1], v[10] * mu, v[11] * mu, 1);
-        cw[1] = FP4Q_ENC2(cw[1], v[12] * mu, v[13] * mu, 2);
-        cw[1] = FP4Q_ENC2(cw[1], v[14] * mu, v[15] * mu, 3);
+#pragma clang loop unroll(full)
+        for (int j = 0; j < kOcts; ++j) cw[j] = rne8(v + 8 * j, s.mul);
       }
-      *reinterpret_cast<uint2*>(codes_c + gc * (rows / 2) + gr0 / 2) = make_uint2(cw[0], cw[1]);
-      scales_c[gc * (rows / 16) + gr0 / 16] = (uint8_t)s.code;
+      store_block_codes<kBlk>(codes_c + gc * (rows / 2) + gr0 / 2, cw);
+      scales_c[gc * (rows / kBlk) + gr0 / kBlk] = (uint8_t)s.code;
       nzero += s.flags & 1u;
       nsat += s.flags >> 1;
     }
@@ -338,7 +378,7 @@ __device__ __forceinline__ void store_col_codes(uint8_t* dst, const uint32_t (&c
 template <bool kBF16, bool kSR, bool kT>
 __global__ __launch_bounds__(kThreads) void quant_tile_kernel(
     const uint8_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld_bytes, int col_groups,
-    int row_groups, const float* __restrict__ amax_held, float target, uint64_t seed,
+    int row_groups, const float* __restrict__ amax_held, float target, int e4m3, uint64_t seed,
     uint32_t subseq, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
     uint8_t* __restrict__ codes_t, uint8_t* __restrict__ scales_t, float* __restrict__ enc_out,
     int32_t* __restrict__ diag) {
@@ -377,7 +417,7 @@ __global__ __launch_bounds__(kThreads) void quant_tile_kernel(
       m = max(m, v[r].absmax());
     }
     m = max(m, (uint32_t)__shfl_xor((int)m, 1));
-    const BlockScale b = block_scale(m, S, S_d);
+    const BlockScale b = block_scale(m, S, S_d, e4m3 != 0);
     const bool mi = __builtin_isinf(b.mul);
 #pragma clang loop unroll(full)
     for (int r = 0; r < 16; ++r) {
@@ -408,48 +448,139 @@ __global__ __launch_bounds__(kThreads) void quant_tile_kernel(
   if (diag) add_diag(diag, nzero, nsat);
 }
 
-template <bool kBF16, bool kSR>
+
+// ------------------------------------------------------------------ TILE32
+// 32 x 32 tiles (the block-32 weight layout). A lane holds 8 columns of one
+// 32-row tile band; four adjacent lanes cover a tile. The band is read twice
+// (once for the tile maxima, once to encode: the second read hits the
+// cache), so a lane keeps one row at a time. The transposed copy gets 16
+// contiguous bytes per column.
+template <bool kBF16, bool kSR, bool kT>
+__global__ __launch_bounds__(kThreads) void quant_tile32_kernel(
+    const uint8_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld_bytes, int col_groups,
+    int row_groups, const float* __restrict__ amax_held, float target, int e4m3, uint64_t seed,
+    uint32_t subseq, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
+    uint8_t* __restrict__ codes_t, uint8_t* __restrict__ scales_t, float* __restrict__ enc_out,
+    int32_t* __restrict__ diag) {
+  constexpr int es = kBF16 ? 2 : 4;
+  const int item = xcd_order(blockIdx.x, col_groups * row_groups);
+  const int cg = item / row_groups;
+  const int rg = item - cg * row_groups;
+  const float S = tensor_scale(*amax_held, target);
+  const double S_d = (double)S;
+  if (enc_out && blockIdx.x == 0 && threadIdx.x == 0) *enc_out = S;
+  const int64_t oct = (int64_t)cg * kThreads + threadIdx.x;
+  const int64_t c0 = oct * 8;
+  const bool valid = c0 < cols;  // equal within a lane quad (cols % 32 == 0)
+  const int64_t r0 = (int64_t)rg * 32;
+  uint32_t m = 0u;
+#pragma clang loop unroll(full)
+  for (int r = 0; r < 32; ++r) {
+    Oct<kBF16> v;
+    if (valid) v.load(x + (r0 + r) * ld_bytes + c0 * es);
+    else v.zero();
+    m = max(m, v.absmax());
+  }
+  m = max(m, (uint32_t)__shfl_xor((int)m, 1));
+  m = max(m, (uint32_t)__shfl_xor((int)m, 2));
+  const BlockScale b = block_scale(m, S, S_d, e4m3 != 0);
+  const bool mi = __builtin_isinf(b.mul);
+  uint32_t tcodes[8][4];
+#pragma clang loop unroll(full)
+  for (int j = 0; j < 8; ++j)
+#pragma clang loop unroll(full)
+    for (int q = 0; q < 4; ++q) tcodes[j][q] = 0u;
+#pragma clang loop unroll(full)
+  for (int r = 0; r < 32; ++r) {
+    Oct<kBF16> v;
+    if (valid) v.load(x + (r0 + r) * ld_bytes + c0 * es);
+    else v.zero();
+    uint32_t w[8];
+    if (kSR) words8((uint64_t)(r0 + r) * (uint64_t)cols + (uint64_t)c0, seed, subseq, w);
+    const uint32_t word = encode_oct<kBF16, kSR>(v, b.mul, mi, w);
+    if (valid) reinterpret_cast<uint32_t*>(codes + (r0 + r) * (cols / 2))[oct] = word;
+    if (kT) {
+#pragma clang loop unroll(full)
+      for (int j = 0; j < 8; ++j) tcodes[j][r >> 3] |= ((word >> (4 * j)) & 0xFu) << (4 * (r & 7));
+    }
+  }
+  uint32_t nzero = 0u, nsat = 0u;
+  if (valid && (threadIdx.x & 3) == 0) {
+    scales[(r0 / 32) * (cols / 32) + (oct >> 2)] = (uint8_t)b.code;
+    if (kT) scales_t[(oct >> 2) * (rows / 32) + r0 / 32] = (uint8_t)b.code;
+    nzero = b.flags & 1u;
+    nsat = b.flags >> 1;
+  }
+  if (kT && valid) {
+#pragma clang loop unroll(full)
+    for (int j = 0; j < 8; ++j) store_block_codes<32>(codes_t + (c0 + j) * (rows / 2) + r0 / 2, tcodes[j]);
+  }
+  if (diag) add_diag(diag, nzero, nsat);
+}
+
+template <bool kBF16, bool kSR, int kBlk>
 hipError_t launch_typed(const QuantArgs& a, hipStream_t s) {
   const uint8_t* x = static_cast<const uint8_t*>(a.x);
   const int64_t ldb = a.ld * a.es;
+  const int e4m3 = a.scale_fmt;
   const bool both = a.layout == 0 && a.codes_t != nullptr;
   if (a.layout == 0 && !both) {
-    const int64_t nblk = a.cols / 16;
+    const int64_t nblk = a.cols / kBlk;
     const int segs = (int)((nblk + kRowThreads - 1) / kRowThreads);
-    hipLaunchKernelGGL((quant_row16_kernel<kBF16, kSR>), dim3((uint32_t)(a.rows * segs)), dim3(kRowThreads),
-                       0, s, x, a.cols, ldb, segs, a.amax_held, a.target, a.seed, a.subseq, a.codes,
-                       a.scales, a.enc_scale_out, a.diag);
+    hipLaunchKernelGGL((quant_row_kernel<kBF16, kSR, kBlk>), dim3((uint32_t)(a.rows * segs)),
+                       dim3(kRowThreads), 0, s, x, a.cols, ldb, segs, a.amax_held, a.target, e4m3,
+                       a.seed, a.subseq, a.codes, a.scales, a.enc_scale_out, a.diag);
     return hipGetLastError();
   }
   if (a.layout == 2) {
     const int col_groups = (int)((a.cols / 8 + kThreads - 1) / kThreads);
+    if (kBlk == 32) {
+      const dim3 grid((uint32_t)(col_groups * (a.rows / 32)));
+      if (a.codes_t)
+        hipLaunchKernelGGL((quant_tile32_kernel<kBF16, kSR, true>), grid, dim3(kThreads), 0, s, x,
+                           a.rows, a.cols, ldb, col_groups, (int)(a.rows / 32), a.amax_held, a.target,
+                           e4m3, a.seed, a.subseq, a.codes, a.scales, a.codes_t, a.scales_t,
+                           a.enc_scale_out, a.diag);
+      else
+        hipLaunchKernelGGL((quant_tile32_kernel<kBF16, kSR, false>), grid, dim3(kThreads), 0, s, x,
+                           a.rows, a.cols, ldb, col_groups, (int)(a.rows / 32), a.amax_held, a.target,
+                           e4m3, a.seed, a.subseq, a.codes, a.scales, nullptr, nullptr,
+                           a.enc_scale_out, a.diag);
+      return hipGetLastError();
+    }
     constexpr int ksub = sub_tiles<kBF16>();
     const int row_groups = (int)((a.rows / 16 + ksub - 1) / ksub);
     const dim3 grid((uint32_t)(col_groups * row_groups));
     if (a.codes_t)
       hipLaunchKernelGGL((quant_tile_kernel<kBF16, kSR, true>), grid, dim3(kThreads), 0, s, x, a.rows,
-                         a.cols, ldb, col_groups, row_groups, a.amax_held, a.target, a.seed, a.subseq,
-                         a.codes, a.scales, a.codes_t, a.scales_t, a.enc_scale_out, a.diag);
+                         a.cols, ldb, col_groups, row_groups, a.amax_held, a.target, e4m3, a.seed,
+                         a.subseq, a.codes, a.scales, a.codes_t, a.scales_t, a.enc_scale_out, a.diag);
     else
       hipLaunchKernelGGL((quant_tile_kernel<kBF16, kSR, false>), grid, dim3(kThreads), 0, s, x, a.rows,
-                         a.cols, ldb, col_groups, row_groups, a.amax_held, a.target, a.seed, a.subseq,
-                         a.codes, a.scales, nullptr, nullptr, a.enc_scale_out, a.diag);
+                         a.cols, ldb, col_groups, row_groups, a.amax_held, a.target, e4m3, a.seed,
+                         a.subseq, a.codes, a.scales, nullptr, nullptr, a.enc_scale_out, a.diag);
     return hipGetLastError();
   }
-  const int col_tiles = (int)((a.cols + kTT - 1) / kTT);
-  const int row_tiles = (int)((a.rows + kTT - 1) / kTT);
-  const dim3 grid((uint32_t)(col_tiles * row_tiles));
+  constexpr int kTC = kDualCols<kBlk>(), kTR = kDualRows<kBlk>();
+  const int col_tiles = (int)((a.cols + kTC - 1) / kTC);
+  const int row_tiles = (int)((a.rows + kTR - 1) / kTR);
+  const dim3 grid((uint32_t)(col_tiles * row_tiles)), block(kDualThreads<kBlk>());
   if (both) {
-    // ROW16 outputs in codes/scales, COL16 outputs in codes_t/scales_t
-    hipLaunchKernelGGL((quant_dual_kernel<kBF16, kSR, true>), grid, dim3(kThreads), 0, s, x, a.rows,
-                       a.cols, ldb, col_tiles, row_tiles, a.amax_held, a.target, a.seed, a.subseq,
-                       a.codes, a.scales, a.codes_t, a.scales_t, a.enc_scale_out, a.diag);
+    // ROW outputs in codes/scales, COL outputs in codes_t/scales_t
+    hipLaunchKernelGGL((quant_dual_kernel<kBF16, kSR, true, kBlk>), grid, block, 0, s, x, a.rows,
+                       a.cols, ldb, col_tiles, row_tiles, a.amax_held, a.target, e4m3, a.seed,
+                       a.subseq, a.codes, a.scales, a.codes_t, a.scales_t, a.enc_scale_out, a.diag);
   } else {
-    hipLaunchKernelGGL((quant_dual_kernel<kBF16, kSR, false>), grid, dim3(kThreads), 0, s, x, a.rows,
-                       a.cols, ldb, col_tiles, row_tiles, a.amax_held, a.target, a.seed, a.subseq,
-                       nullptr, nullptr, a.codes, a.scales, a.enc_scale_out, a.diag);
+    hipLaunchKernelGGL((quant_dual_kernel<kBF16, kSR, false, kBlk>), grid, block, 0, s, x, a.rows,
+                       a.cols, ldb, col_tiles, row_tiles, a.amax_held, a.target, e4m3, a.seed,
+                       a.subseq, nullptr, nullptr, a.codes, a.scales, a.enc_scale_out, a.diag);
   }
   return hipGetLastError();
+}
+
+template <bool kBF16, bool kSR>
+hipError_t launch_block(const QuantArgs& a, hipStream_t s) {
+  return a.block == 32 ? launch_typed<kBF16, kSR, 32>(a, s) : launch_typed<kBF16, kSR, 16>(a, s);
 }
 
 }  // namespace
@@ -462,8 +593,8 @@ hipError_t launch_quantize(const QuantArgs& a, hipStream_t s) {
                          a.enc_scale_out);
     return hipGetLastError();
   }
-  if (a.es == 2) return a.sr ? launch_typed<true, true>(a, s) : launch_typed<true, false>(a, s);
-  return a.sr ? launch_typed<false, true>(a, s) : launch_typed<false, false>(a, s);
+  if (a.es == 2) return a.sr ? launch_block<true, true>(a, s) : launch_block<true, false>(a, s);
+  return a.sr ? launch_block<false, true>(a, s) : launch_block<false, false>(a, s);
 }
 
 }  // namespace fp4q

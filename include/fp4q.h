@@ -32,7 +32,7 @@
 extern "C" {
 #endif
 
-#define FP4Q_ABI_VERSION 1
+#define FP4Q_ABI_VERSION 2
 
 typedef enum {
     FP4Q_OK = 0,
@@ -53,7 +53,9 @@ typedef enum { FP4Q_F32 = 0, FP4Q_BF16 = 1 } fp4q_dtype;
 typedef enum { FP4Q_RNE = 0, FP4Q_SR = 1 } fp4q_round;
 
 /* Block geometry (§3 and §5 of the page: 1D blocks of 16 along the
- * contraction axis for activations and gradients, 2D 16x16 for weights). */
+ * contraction axis for activations and gradients, 2D 16x16 for weights).
+ * The names give the default block of 16; with a block size B of 32 (the
+ * page's block-32 run, §7.3) every 16 below reads B. */
 typedef enum {
     FP4Q_ROW16 = 0,     /* blocks of 16 along a row; codes [R][C/2], scales [R][C/16] */
     FP4Q_COL16 = 1,     /* blocks of 16 down a column, stored as ROW16 of the
@@ -61,12 +63,17 @@ typedef enum {
     FP4Q_TILE16x16 = 2  /* 16x16 tiles; codes [R][C/2], scales [R/16][C/16] */
 } fp4q_layout;
 
+/* Block-scale format: UE5M3 (the page's, §4.1) or E4M3 (NVFP4's, §3; codes
+ * 0x00..0x7E: 2^-9 .. 448, the same code's UE5M3 value times 256). */
+typedef enum { FP4Q_UE5M3 = 0, FP4Q_E4M3 = 1 } fp4q_scale_fmt;
+
 /* One quantized operand as the GEMMs read it: `rows` x `cols` logical
  * elements, contiguous along `cols` (the contraction). layout is FP4Q_ROW16
- * (scales [rows][cols/16]; also what FP4Q_COL16 produces for the transpose)
- * or FP4Q_TILE16x16 (scales [rows/16][cols/16]). enc_scale points to the
- * device fp32 tensor scale S written by fp4q_quantize. codes must be 8-byte
- * aligned and scales 4-byte aligned. */
+ * (scales [rows][cols/B]; also what FP4Q_COL16 produces for the transpose)
+ * or FP4Q_TILE16x16 (scales [rows/B][cols/B]), B = block (16 or 32);
+ * scale_fmt an fp4q_scale_fmt. enc_scale points to the device fp32 tensor
+ * scale S written by fp4q_quantize. codes must be 8-byte aligned and scales
+ * 4-byte aligned. */
 typedef struct {
     const uint8_t *codes;
     const uint8_t *scales;
@@ -74,6 +81,8 @@ typedef struct {
     int64_t rows;
     int64_t cols;
     int32_t layout;
+    int32_t block;
+    int32_t scale_fmt;
 } fp4q_qtensor;
 
 int fp4q_abi_version(void);
@@ -130,10 +139,26 @@ fp4q_status fp4q_quantize(const void *x, fp4q_dtype xt, int64_t rows, int64_t co
                           uint8_t *scales_t, int32_t *diag, void *stream);
 
 /*
+ * fp4q_quantize with a block size (16 or 32) and a scale format
+ * (fp4q_scale_fmt): the page's block-32 variant and NVFP4's E4M3 scales
+ * (§3, §7.3). Every rule above carries over with B = block in place of 16
+ * (shapes, divisibility, the TILE transposed copy with B x B tiles, the ROW
+ * plus COL single pass); for E4M3 the nearest-code encode saturates once raw
+ * exceeds 464 (to 0x7E = 448) and a zero-rounded scale repairs to 0x01
+ * (2^-9). fp4q_quantize is this call with block 16 and FP4Q_UE5M3.
+ */
+fp4q_status fp4q_quantize_fmt(const void *x, fp4q_dtype xt, int64_t rows, int64_t cols,
+                              int64_t ld, const float *amax_held, float target,
+                              fp4q_layout layout, int32_t block, fp4q_scale_fmt scale_fmt,
+                              fp4q_round rnd, uint64_t seed, uint32_t subseq, uint8_t *codes,
+                              uint8_t *scales, float *enc_scale_out, uint8_t *codes_t,
+                              uint8_t *scales_t, int32_t *diag, void *stream);
+
+/*
  * Dequantize q into out ([q->rows, q->cols], row-major, dtype ot):
  * x_hat = RN_fp32((e2m1 * dec) / S), then RNE to bf16 for FP4Q_BF16 (§6 of
  * the page: the emulation decodes operands exactly; S is removed after).
- * q->cols % 16 == 0; out 16-byte aligned.
+ * q->cols % q->block == 0; out 16-byte aligned.
  */
 fp4q_status fp4q_dequant(const fp4q_qtensor *q, void *out, fp4q_dtype ot, void *stream);
 
@@ -148,7 +173,9 @@ fp4q_status fp4q_dequant(const fp4q_qtensor *q, void *out, fp4q_dtype ot, void *
  *  wgrad: dw[N, K] = dYq^T[N, M] . Xq[M, K]     dyqt: dY COL16 ([N, M] stored);
  *                                               xqt:  X COL16 ([K, M] stored)
  * In each, both operands must have equal `cols` (the contraction length,
- * a multiple of 16) and `rows` a multiple of 16 when their layout is TILE.
+ * a multiple of 16 and of each operand's block size) and `rows` a multiple of
+ * the block size when their layout is TILE. The two operands may use
+ * different block sizes and scale formats.
  */
 fp4q_status fp4q_linear_fwd(const fp4q_qtensor *xq, const fp4q_qtensor *wq, void *y,
                             fp4q_dtype yt, void *stream);

@@ -30,13 +30,15 @@ _SRC = os.path.join(_HERE, "fp4q_oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
 F32, BF16 = 0, 1
-ROW16, COL16, TILE16 = 0, 1, 2
+ROW16, COL16, TILE16 = 0, 1, 2   # blocks along a row, down a column, square tiles
 RNE, SR = 0, 1
+UE5M3, E4M3 = 0, 1               # block-scale formats
 
 
 def build(force: bool = True) -> str:
     """Compile the oracle with gcc (plain IEEE binary32, no FMA contraction)."""
-    if force or not os.path.exists(_LIB):
+    stale = os.path.exists(_LIB) and os.path.getmtime(_SRC) > os.path.getmtime(_LIB)
+    if force or stale or not os.path.exists(_LIB):
         tmp = _LIB + ".tmp"
         cmd = ["gcc", "-O2", "-std=gnu11", "-ffp-contract=off", "-fno-fast-math", "-frounding-math",
                "-fPIC", "-shared", "-o", tmp, _SRC, "-lm"]
@@ -62,6 +64,10 @@ def lib():
         L.oracle_ue5m3_encode.argtypes = [c_f, ctypes.POINTER(ctypes.c_int)]
         L.oracle_ue5m3_nearest.restype = ctypes.c_int
         L.oracle_ue5m3_nearest.argtypes = [c_f]
+        L.oracle_e4m3_decode.restype = c_d
+        L.oracle_e4m3_decode.argtypes = [ctypes.c_int]
+        L.oracle_e4m3_encode.restype = ctypes.c_int
+        L.oracle_e4m3_encode.argtypes = [c_f, ctypes.POINTER(ctypes.c_int)]
         L.oracle_e2m1_encode_rne.restype = ctypes.c_int
         L.oracle_e2m1_encode_rne.argtypes = [c_f, ctypes.c_int]
         L.oracle_e2m1_encode_sr.restype = ctypes.c_int
@@ -78,6 +84,15 @@ def lib():
         L.oracle_quantize.argtypes = [c_p, ctypes.c_int, c_i64, c_i64, c_i64, c_f, c_f,
                                       ctypes.c_int, ctypes.c_int, ctypes.c_uint64, ctypes.c_uint32,
                                       c_i64, c_i64, c_i64, c_p, c_p, c_p, c_p, c_p, c_p]
+        L.oracle_quantize_fmt.restype = ctypes.c_int
+        L.oracle_quantize_fmt.argtypes = [c_p, ctypes.c_int, c_i64, c_i64, c_i64, c_f, c_f, ctypes.c_int,
+                                          ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_uint64,
+                                          ctypes.c_uint32, c_i64, c_i64, c_i64, c_p, c_p, c_p, c_p, c_p, c_p]
+        L.oracle_decode_f64_fmt.restype = None
+        L.oracle_decode_f64_fmt.argtypes = [c_p, c_p, c_i64, c_i64, ctypes.c_int, ctypes.c_int, ctypes.c_int, c_p]
+        L.oracle_dequant_f32_fmt.restype = None
+        L.oracle_dequant_f32_fmt.argtypes = [c_p, c_p, c_i64, c_i64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                             c_f, c_p]
         L.oracle_decode_f64.restype = None
         L.oracle_decode_f64.argtypes = [c_p, c_p, c_i64, c_i64, ctypes.c_int, c_p]
         L.oracle_dequant_f32.restype = None
@@ -148,6 +163,17 @@ def sr_word(seed: int, subseq: int, index: int) -> int:
     return lib().oracle_sr_word(int(seed), int(subseq), int(index))
 
 
+def e4m3_decode(code: int) -> float:
+    return lib().oracle_e4m3_decode(int(code))
+
+
+def e4m3_encode(raw: float) -> tuple[int, int]:
+    """(code, flags) of the E4M3 block-scale encode with repair."""
+    f = ctypes.c_int(0)
+    c = lib().oracle_e4m3_encode(float(raw), ctypes.byref(f))
+    return c, f.value
+
+
 def tensor_scale(amax: float, T: float) -> np.float32:
     return np.float32(lib().oracle_tensor_scale(float(amax), float(T)))
 
@@ -163,11 +189,13 @@ def amax(x: np.ndarray) -> np.float32:
 class QTensor:
     """A quantized operand stored contiguous along its contraction (cols)."""
     codes: np.ndarray      # uint8 [rows, cols/2]
-    scales: np.ndarray     # uint8 ROW16 [rows, cols/16]; TILE16 [rows/16, cols/16]
+    scales: np.ndarray     # uint8 ROW16 [rows, cols/block]; TILE16 [rows/block, cols/block]
     S: np.float32          # tensor (encode) scale
     rows: int
     cols: int
     layout: int            # ROW16 or TILE16
+    block: int = 16        # block size (16, or 32 for the block-32 variant)
+    scale_fmt: int = UE5M3  # UE5M3, or E4M3 (NVFP4's scale format)
 
 
 @dataclass
@@ -179,57 +207,59 @@ class Quantized:
 
 def quantize(x: np.ndarray, amax_held: float, T: float = 448.0, layout: int = ROW16,
              rnd: int = RNE, seed: int = 0, subseq: int = 0, transposed: bool = False,
-             origin: tuple | None = None) -> Quantized:
+             origin: tuple | None = None, block: int = 16, scale_fmt: int = UE5M3) -> Quantized:
     """Quantize x. ``origin = (row0, col0, full_cols)`` places x inside a
     larger logical tensor for the SR word index (default: x is the whole
-    tensor)."""
+    tensor). ``block`` (16 or 32) and ``scale_fmt`` (UE5M3 or E4M3) select
+    the block geometry and the block-scale format."""
     xc, dt = _as_input(x)
     rows, cols = xc.shape
+    B = block
     row0, col0, full_cols = origin if origin is not None else (0, 0, cols)
-    if (layout != COL16 and cols % 16) or (layout != ROW16 and rows % 16):
-        raise ValueError("the blocked dimension(s) must be multiples of 16")
+    if B not in (16, 32) or (layout != COL16 and cols % B) or (layout != ROW16 and rows % B):
+        raise ValueError("the blocked dimension(s) must be multiples of the block size (16 or 32)")
     if layout == COL16:
         codes = np.zeros((cols, rows // 2), np.uint8)
-        scales = np.zeros((cols, rows // 16), np.uint8)
+        scales = np.zeros((cols, rows // B), np.uint8)
     else:
         codes = np.zeros((rows, cols // 2), np.uint8)
-        scales = np.zeros((rows, cols // 16) if layout == ROW16 else (rows // 16, cols // 16), np.uint8)
+        scales = np.zeros((rows, cols // B) if layout == ROW16 else (rows // B, cols // B), np.uint8)
     codes_t = scales_t = None
     if layout == TILE16 and transposed:
         codes_t = np.zeros((cols, rows // 2), np.uint8)
-        scales_t = np.zeros((cols // 16, rows // 16), np.uint8)
+        scales_t = np.zeros((cols // B, rows // B), np.uint8)
     S = np.zeros(1, np.float32)
     diag = np.zeros(2, np.int32)
-    rc = lib().oracle_quantize(_ptr(xc), dt, rows, cols, cols, float(amax_held), float(T), layout, rnd,
-                               int(seed), int(subseq), int(row0), int(col0), int(full_cols),
-                               _ptr(codes), _ptr(scales), _ptr(S),
-                               _ptr(codes_t) if codes_t is not None else None,
-                               _ptr(scales_t) if scales_t is not None else None, _ptr(diag))
+    rc = lib().oracle_quantize_fmt(_ptr(xc), dt, rows, cols, cols, float(amax_held), float(T), layout,
+                                   B, scale_fmt, rnd, int(seed), int(subseq), int(row0), int(col0),
+                                   int(full_cols), _ptr(codes), _ptr(scales), _ptr(S),
+                                   _ptr(codes_t) if codes_t is not None else None,
+                                   _ptr(scales_t) if scales_t is not None else None, _ptr(diag))
     if rc != 0:
-        raise ValueError("oracle_quantize: bad shape")
+        raise ValueError("oracle_quantize: bad shape or format")
     if layout == COL16:
-        q = QTensor(codes, scales, S[0], cols, rows, ROW16)
+        q = QTensor(codes, scales, S[0], cols, rows, ROW16, B, scale_fmt)
     else:
-        q = QTensor(codes, scales, S[0], rows, cols, layout)
+        q = QTensor(codes, scales, S[0], rows, cols, layout, B, scale_fmt)
     qt = None
     if codes_t is not None:
-        qt = QTensor(codes_t, scales_t, S[0], cols, rows, TILE16)
+        qt = QTensor(codes_t, scales_t, S[0], cols, rows, TILE16, B, scale_fmt)
     return Quantized(q, qt, diag)
 
 
 def decode_f64(q: QTensor) -> np.ndarray:
     """e2m1(code) * dec(scale) per element, exact in float64 (no tensor scale)."""
     out = np.zeros((q.rows, q.cols), np.float64)
-    lib().oracle_decode_f64(_ptr(np.ascontiguousarray(q.codes)), _ptr(np.ascontiguousarray(q.scales)),
-                            q.rows, q.cols, q.layout, _ptr(out))
+    lib().oracle_decode_f64_fmt(_ptr(np.ascontiguousarray(q.codes)), _ptr(np.ascontiguousarray(q.scales)),
+                                q.rows, q.cols, q.layout, q.block, q.scale_fmt, _ptr(out))
     return out
 
 
 def dequant_f32(q: QTensor) -> np.ndarray:
     """x_hat = RN_f32((e2m1 * dec) / S)."""
     out = np.zeros((q.rows, q.cols), np.float32)
-    lib().oracle_dequant_f32(_ptr(np.ascontiguousarray(q.codes)), _ptr(np.ascontiguousarray(q.scales)),
-                             q.rows, q.cols, q.layout, float(q.S), _ptr(out))
+    lib().oracle_dequant_f32_fmt(_ptr(np.ascontiguousarray(q.codes)), _ptr(np.ascontiguousarray(q.scales)),
+                                 q.rows, q.cols, q.layout, q.block, q.scale_fmt, float(q.S), _ptr(out))
     return out
 
 

@@ -112,9 +112,10 @@ static int ue5m3_nearest_prerepair(float raw)
 }
 
 /*
- * Scale encode with repair. READING of [UE5M3] §5.3, which speaks of
- * "pre-repair zero-rounded or saturated scale codes": a scale that rounds to
- * zero for a non-zero block becomes the smallest positive code 0x01; a scale
+ * Scale encode with repair. READING of [UE5M3] §5.3, which counts scale
+ * codes that were zero-rounded or saturated before repair: a scale that
+ * rounds to zero for a non-zero block becomes the smallest positive code
+ * 0x01; a scale
  * that rounds above the largest finite value becomes 0xF7 (61,440).
  * flags bit 0: zero-rounded before repair, bit 1: saturated before repair.
  */
@@ -138,8 +139,80 @@ int oracle_ue5m3_encode(float raw, int *flags)
 int oracle_ue5m3_nearest(float raw) { return ue5m3_nearest_prerepair(raw); }
 
 /* ------------------------------------------------------------------------
+ * E4M3 block scale, NVFP4's ([UE5M3] §3; §4.1 compares it with UE5M3): one
+ * sign bit, four exponent bits with bias 7, three fraction bits; exponent
+ * field 15 with fraction 7 is NaN, so the largest finite value is 448 and the
+ * smallest subnormal 2^-9 (the ratios 61,440 / 448 ~ 137 and 2^-9 / 2^-17 =
+ * 256 that §4.1 prints). Block scales are non-negative: codes 0x00..0x7E.
+ * Encode and repair follow the UE5M3 rules above: nearest with ties to the
+ * even code, a scale rounding to zero becomes 0x01 (2^-9), one rounding
+ * above 448 (the next point of an unbounded codebook being 480) becomes
+ * 0x7E.
+ * ---------------------------------------------------------------------- */
+double oracle_e4m3_decode(int code)
+{
+    int sgn = (code >> 7) & 1;
+    int e = (code >> 3) & 15;
+    int m = code & 7;
+    if (e == 15 && m == 7)
+        return NAN;
+    double v = (e == 0) ? m * ldexp(1.0, -9) : (1.0 + m / 8.0) * ldexp(1.0, e - 7);
+    return sgn ? -v : v;
+}
+
+#define E4M3_MAX_FINITE_CODE 0x7E
+#define E4M3_BEYOND_MAX 480.0
+
+static int e4m3_nearest_prerepair(float raw)
+{
+    double x = raw;
+    if (x > E4M3_BEYOND_MAX)
+        return 0x7F;
+    int best = 0;
+    double bestd = fabs(x);
+    for (int c = 1; c <= 0x7F; ++c) {
+        double v = (c == 0x7F) ? E4M3_BEYOND_MAX : oracle_e4m3_decode(c);
+        double d = fabs(x - v);
+        if (d < bestd || (d == bestd && (c & 1) == 0)) {
+            best = c;
+            bestd = d;
+        }
+    }
+    return best;
+}
+
+int oracle_e4m3_encode(float raw, int *flags)
+{
+    int c = e4m3_nearest_prerepair(raw);
+    int f = 0;
+    if (c == 0) {
+        c = 0x01;
+        f |= 1;
+    } else if (c == 0x7F) {
+        c = E4M3_MAX_FINITE_CODE;
+        f |= 2;
+    }
+    if (flags)
+        *flags = f;
+    return c;
+}
+
+#define ORACLE_UE5M3 0
+#define ORACLE_E4M3 1
+
+static double scale_decode(int fmt, int code)
+{
+    return fmt == ORACLE_E4M3 ? oracle_e4m3_decode(code) : oracle_ue5m3_decode(code);
+}
+
+static int scale_encode(int fmt, float raw, int *flags)
+{
+    return fmt == ORACLE_E4M3 ? oracle_e4m3_encode(raw, flags) : oracle_ue5m3_encode(raw, flags);
+}
+
+/* ------------------------------------------------------------------------
  * E2M1 payload rounding.
- * RNE: [UE5M3] §2 ("nearest-even" saved activations) and [RPS] App. A.2
+ * RNE: [UE5M3] §2 (saved activations rounded to nearest even) and [RPS] App. A.2
  * (RTN with a predetermined tie rule; here: the even code). Values beyond
  * the largest magnitude saturate to 6 ([UE5M3] §3: oversized values
  * saturate). READING: a NaN scaled value, which only arises as 0 * Inf when
@@ -310,6 +383,10 @@ float oracle_tensor_scale(float amax, float T)
  *                   the same codes and scales transposed.
  * Packing: byte k of a stored row holds its elements 2k (bits 3:0) and
  * 2k+1 (bits 7:4).
+ * Variants (block size 32, E4M3 scales: the page's block-32 run and NVFP4's
+ * scale format, [UE5M3] §3 and §7.3) go through oracle_quantize_fmt: blocks
+ * of `block` elements (a row or column segment, or block x block tiles) and
+ * the scale format's encode/decode; shapes scale by `block` instead of 16.
  * Per block ([UE5M3] §3-§5; READING for the binary32 order of operations):
  *   bamax = max |x| over the block
  *   bamax == 0 : scale code 0, every payload code is the element's sign bit
@@ -333,17 +410,19 @@ static void put_code(uint8_t *codes, int64_t stride_bytes, int64_t row, int64_t 
         *b = (uint8_t)((*b & 0xF0) | code);
 }
 
-int oracle_quantize(const void *x, int dtype, int64_t rows, int64_t cols, int64_t ld,
-                    float amax_held, float T, int layout, int rnd, uint64_t seed, uint32_t subseq,
-                    int64_t idx_row0, int64_t idx_col0, int64_t idx_cols,
-                    uint8_t *codes, uint8_t *scales, float *enc_scale_out,
-                    uint8_t *codes_t, uint8_t *scales_t, int32_t *diag)
+int oracle_quantize_fmt(const void *x, int dtype, int64_t rows, int64_t cols, int64_t ld,
+                        float amax_held, float T, int layout, int block, int scale_fmt, int rnd,
+                        uint64_t seed, uint32_t subseq, int64_t idx_row0, int64_t idx_col0,
+                        int64_t idx_cols, uint8_t *codes, uint8_t *scales, float *enc_scale_out,
+                        uint8_t *codes_t, uint8_t *scales_t, int32_t *diag)
 {
     /* The blocked dimension(s) must hold whole blocks; the other may be
      * ragged (any length, including 0). */
-    if (rows < 0 || cols < 0 || ld < cols)
+    if (rows < 0 || cols < 0 || ld < cols || (block != 16 && block != 32))
         return -1;
-    if ((layout != ORACLE_COL16 && cols % 16) || (layout != ORACLE_ROW16 && rows % 16))
+    if (scale_fmt != ORACLE_UE5M3 && scale_fmt != ORACLE_E4M3)
+        return -1;
+    if ((layout != ORACLE_COL16 && cols % block) || (layout != ORACLE_ROW16 && rows % block))
         return -1;
     float S = oracle_tensor_scale(amax_held, T);
     if (enc_scale_out)
@@ -351,8 +430,8 @@ int oracle_quantize(const void *x, int dtype, int64_t rows, int64_t cols, int64_
     int32_t nzero = 0, nsat = 0;
 
     /* Block extent: br x bc elements starting at (r0, c0). */
-    int64_t br = (layout == ORACLE_ROW16) ? 1 : 16;
-    int64_t bc = (layout == ORACLE_COL16) ? 1 : 16;
+    int64_t br = (layout == ORACLE_ROW16) ? 1 : block;
+    int64_t bc = (layout == ORACLE_COL16) ? 1 : block;
     for (int64_t r0 = 0; r0 < rows; r0 += br) {
         for (int64_t c0 = 0; c0 < cols; c0 += bc) {
             float bamax = 0.0f;
@@ -368,10 +447,10 @@ int oracle_quantize(const void *x, int dtype, int64_t rows, int64_t cols, int64_
                 float d6 = bamax / 6.0f;
                 float raw = d6 * S;
                 int flags = 0;
-                scode = oracle_ue5m3_encode(raw, &flags);
+                scode = scale_encode(scale_fmt, raw, &flags);
                 nzero += flags & 1;
                 nsat += (flags >> 1) & 1;
-                float dec = (float)oracle_ue5m3_decode(scode);
+                float dec = (float)scale_decode(scale_fmt, scode);
                 r_mul = S / dec;
             }
             for (int64_t r = r0; r < r0 + br; ++r)
@@ -398,13 +477,13 @@ int oracle_quantize(const void *x, int dtype, int64_t rows, int64_t cols, int64_
                     }
                 }
             if (layout == ORACLE_ROW16)
-                scales[r0 * (cols / 16) + c0 / 16] = (uint8_t)scode;
+                scales[r0 * (cols / block) + c0 / block] = (uint8_t)scode;
             else if (layout == ORACLE_COL16)
-                scales[c0 * (rows / 16) + r0 / 16] = (uint8_t)scode;
+                scales[c0 * (rows / block) + r0 / block] = (uint8_t)scode;
             else {
-                scales[(r0 / 16) * (cols / 16) + c0 / 16] = (uint8_t)scode;
+                scales[(r0 / block) * (cols / block) + c0 / block] = (uint8_t)scode;
                 if (scales_t)
-                    scales_t[(c0 / 16) * (rows / 16) + r0 / 16] = (uint8_t)scode;
+                    scales_t[(c0 / block) * (rows / block) + r0 / block] = (uint8_t)scode;
             }
         }
     }
@@ -415,44 +494,65 @@ int oracle_quantize(const void *x, int dtype, int64_t rows, int64_t cols, int64_
     return 0;
 }
 
+int oracle_quantize(const void *x, int dtype, int64_t rows, int64_t cols, int64_t ld,
+                    float amax_held, float T, int layout, int rnd, uint64_t seed, uint32_t subseq,
+                    int64_t idx_row0, int64_t idx_col0, int64_t idx_cols,
+                    uint8_t *codes, uint8_t *scales, float *enc_scale_out,
+                    uint8_t *codes_t, uint8_t *scales_t, int32_t *diag)
+{
+    return oracle_quantize_fmt(x, dtype, rows, cols, ld, amax_held, T, layout, 16, ORACLE_UE5M3,
+                               rnd, seed, subseq, idx_row0, idx_col0, idx_cols, codes, scales,
+                               enc_scale_out, codes_t, scales_t, diag);
+}
+
 /*
  * Decoded operand of a stored quantized tensor ([UE5M3] §6: the emulated
  * GEMM contracts decoded operands): out[r][c] = e2m1(code) * dec(scale),
  * exact in double (at most 6 significant bits). layout is ROW16 or TILE16
  * (a COL16 result is stored as ROW16 of the transpose).
  */
-static double decoded(const uint8_t *codes, const uint8_t *scales, int64_t rows, int64_t cols,
-                      int layout, int64_t r, int64_t c)
+static double decoded(const uint8_t *codes, const uint8_t *scales, int64_t cols, int layout,
+                      int block, int scale_fmt, int64_t r, int64_t c)
 {
     uint8_t byte = codes[r * (cols / 2) + c / 2];
     int q = (c & 1) ? (byte >> 4) : (byte & 0x0F);
-    int sc = (layout == ORACLE_TILE16) ? scales[(r / 16) * (cols / 16) + c / 16]
-                                       : scales[r * (cols / 16) + c / 16];
-    (void)rows;
-    return oracle_e2m1_decode(q) * oracle_ue5m3_decode(sc);
+    int sc = (layout == ORACLE_TILE16) ? scales[(r / block) * (cols / block) + c / block]
+                                       : scales[r * (cols / block) + c / block];
+    return oracle_e2m1_decode(q) * scale_decode(scale_fmt, sc);
+}
+
+void oracle_decode_f64_fmt(const uint8_t *codes, const uint8_t *scales, int64_t rows, int64_t cols,
+                           int layout, int block, int scale_fmt, double *out)
+{
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t c = 0; c < cols; ++c)
+            out[r * cols + c] = decoded(codes, scales, cols, layout, block, scale_fmt, r, c);
 }
 
 void oracle_decode_f64(const uint8_t *codes, const uint8_t *scales, int64_t rows, int64_t cols,
                        int layout, double *out)
 {
-    for (int64_t r = 0; r < rows; ++r)
-        for (int64_t c = 0; c < cols; ++c)
-            out[r * cols + c] = decoded(codes, scales, rows, cols, layout, r, c);
+    oracle_decode_f64_fmt(codes, scales, rows, cols, layout, 16, ORACLE_UE5M3, out);
 }
 
 /*
- * Dequantize to binary32: x_hat = RN((e2m1 * dec) / S), one rounding of an
- * exact product. (A bfloat16 output is this value rounded once more, to
- * bfloat16, by the caller.)
+ * Dequantize to binary32 ([UE5M3] §6): x_hat = RN((e2m1 * dec) / S), one
+ * rounding of an exact product. (A bfloat16 output is this value rounded
+ * once more, to bfloat16, by the caller.)
  */
+void oracle_dequant_f32_fmt(const uint8_t *codes, const uint8_t *scales, int64_t rows, int64_t cols,
+                            int layout, int block, int scale_fmt, float S, float *out)
+{
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t c = 0; c < cols; ++c)
+            out[r * cols + c] =
+                (float)decoded(codes, scales, cols, layout, block, scale_fmt, r, c) / S;
+}
+
 void oracle_dequant_f32(const uint8_t *codes, const uint8_t *scales, int64_t rows, int64_t cols,
                         int layout, float S, float *out)
 {
-    for (int64_t r = 0; r < rows; ++r)
-        for (int64_t c = 0; c < cols; ++c) {
-            float p = (float)decoded(codes, scales, rows, cols, layout, r, c);
-            out[r * cols + c] = p / S;
-        }
+    oracle_dequant_f32_fmt(codes, scales, rows, cols, layout, 16, ORACLE_UE5M3, S, out);
 }
 
 /*

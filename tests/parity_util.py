@@ -25,7 +25,8 @@ def dev_scalar(v: float) -> torch.Tensor:
 
 
 def quant_both(x: torch.Tensor, amax_held: float, layout: str, rnd: int = 0, T: float = 448.0,
-               seed: int = 0, subseq: int = 0, transposed: bool = False, ld_pad: int = 0):
+               seed: int = 0, subseq: int = 0, transposed: bool = False, ld_pad: int = 0,
+               block: int = 16, scale_fmt: int = 0):
     """Quantize the CPU tensor x on the GPU and with the oracle.
 
     Returns (gpu dict of numpy arrays, oracle Quantized). ld_pad > 0 stores x
@@ -38,17 +39,19 @@ def quant_both(x: torch.Tensor, amax_held: float, layout: str, rnd: int = 0, T: 
     else:
         xd = x.to(DEV)
     q, qt, diag = api.quantize(xd, dev_scalar(amax_held), T, lay_g, rnd, seed, subseq,
-                               transposed=transposed, with_diag=True)
+                               transposed=transposed, with_diag=True, block=block, scale_fmt=scale_fmt)
     torch.cuda.synchronize()
     g = dict(codes=q.codes.cpu().numpy(), scales=q.scales.cpu().numpy(),
              S=q.enc_scale.cpu().numpy()[0], diag=diag.cpu().numpy(), q=q, qt=qt)
     if qt is not None:
         g["codes_t"] = qt.codes.cpu().numpy()
         g["scales_t"] = qt.scales.cpu().numpy()
-    o = oracle.quantize(host_view(x), amax_held, T, lay_o, rnd, seed, subseq, transposed=transposed)
+    o = oracle.quantize(host_view(x), amax_held, T, lay_o, rnd, seed, subseq, transposed=transposed,
+                        block=block, scale_fmt=scale_fmt)
     if layout == "row16" and transposed:
         # the second orientation of a ROW16 call is the COL16 quantization
-        oc = oracle.quantize(host_view(x), amax_held, T, oracle.COL16, rnd, seed, subseq)
+        oc = oracle.quantize(host_view(x), amax_held, T, oracle.COL16, rnd, seed, subseq, block=block,
+                             scale_fmt=scale_fmt)
         o.qt = oc.q
         o.diag = o.diag + oc.diag
     return g, o

@@ -28,14 +28,14 @@ def test_library_exports_every_declared_function():
     assert set(names) == set(_lib.EXPORTS), names
     for n in names:
         assert hasattr(L, n), n
-    assert L.fp4q_abi_version() == 1
+    assert L.fp4q_abi_version() == 2
     for s in range(7):
         assert L.fp4q_status_str(s)
 
 
-def q(rows, cols, layout=_lib.ROW16, codes=FAKE, scales=FAKE, S=FAKE):
+def q(rows, cols, layout=_lib.ROW16, codes=FAKE, scales=FAKE, S=FAKE, block=16, fmt=_lib.UE5M3):
     return _lib.QTensorC(codes.value if codes else None, scales.value if scales else None,
-                         S.value if S else None, rows, cols, layout)
+                         S.value if S else None, rows, cols, layout, block, fmt)
 
 
 def quant(**kw):
@@ -112,3 +112,24 @@ def test_probe_gemm_validation():
     assert L.fp4q_linear_probe(a, q(48, 80, _lib.TILE16x16), FAKE, _lib.F32, 10, None) == _lib.E_SHAPE
     assert L.fp4q_linear_probe(a, b, FAKE, 7, 10, None) == _lib.E_DTYPE
     assert L.fp4q_linear_probe(a, b, None, _lib.BF16, 10, None) == _lib.E_NULL
+
+
+def test_format_validation():
+    L = _lib.lib()
+    a, b = q(32, 64), q(48, 64, _lib.TILE16x16)
+    # operand block size / scale format
+    assert L.fp4q_linear_fwd(q(32, 64, block=8), b, FAKE, _lib.BF16, None) == _lib.E_ARG
+    assert L.fp4q_linear_fwd(a, q(48, 64, _lib.TILE16x16, fmt=2), FAKE, _lib.BF16, None) == _lib.E_ARG
+    assert L.fp4q_linear_fwd(q(32, 48, block=32), q(48, 48), FAKE, _lib.BF16, None) == _lib.E_SHAPE
+    assert L.fp4q_linear_fwd(a, q(48, 64, _lib.TILE16x16, block=32), FAKE, _lib.BF16, None) == _lib.E_SHAPE
+    assert L.fp4q_dequant(q(32, 48, block=32), FAKE, _lib.F32, None) == _lib.E_SHAPE
+
+    def qf(rows=64, cols=64, layout=_lib.ROW16, block=32, fmt=_lib.E4M3, ct=None, st=None):
+        return L.fp4q_quantize_fmt(FAKE, _lib.BF16, rows, cols, cols, FAKE, 448.0, layout, block, fmt,
+                                   _lib.RNE, 0, 0, FAKE, FAKE, None, ct, st, None, None)
+    assert qf(block=24) == _lib.E_ARG
+    assert qf(fmt=3) == _lib.E_ARG
+    assert qf(cols=48) == _lib.E_SHAPE                       # ROW blocks of 32
+    assert qf(rows=48, layout=_lib.COL16) == _lib.E_SHAPE    # COL blocks of 32
+    assert qf(rows=48, layout=_lib.TILE16x16) == _lib.E_SHAPE
+    assert qf(rows=48, ct=FAKE, st=FAKE) == _lib.E_SHAPE     # ROW + COL needs rows % 32

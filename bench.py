@@ -227,8 +227,44 @@ def main():
         raise RuntimeError("quantize replayed from a graph differs from the eager call")
     q_bytes = Mq * Kq * (2 + 0.5 + 1 / 16)
     q_gbs = q_bytes / (q_us * 1e-6) / 1e9
-    del Xrot
     log(args, f"quantize-only 8192x4096: {q_us:.2f} us, {q_gbs:.0f} GB/s")
+
+    # the block-32 and E4M3-scale variants: quantize-only (same workload,
+    # graph replay) and the forward GEMM on the FFN shape with variant operands
+    variants = {}
+    for block, fmt, tag in ((32, api.UE5M3, "block32_ue5m3"), (16, api.E4M3, "block16_e4m3"),
+                            (32, api.E4M3, "block32_e4m3")):
+        vc = torch.empty((Mq, Kq // 2), **u8)
+        vs = torch.empty((Mq, Kq // block), **u8)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            for i in range(reps):
+                api.fp4q_quantize_fmt(Xrot[i % nrot], held, T, api.ROW16, block, fmt, api.RNE, 0, 0,
+                                      vc, vs, qS)
+        g.replay()
+        torch.cuda.synchronize()
+        a.record()
+        g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        v_us = a.elapsed_time(b) / reps * 1e3
+        v_bytes = Mq * Kq * (2 + 0.5 + 1 / block)
+        xv, _, _ = api.quantize(X, amax["X"], T, api.ROW16, block=block, scale_fmt=fmt)
+        wv, _, _ = api.quantize(W, amax["W"], T, api.TILE16x16, block=block, scale_fmt=fmt)
+        api.fp4q_linear_fwd(xv, wv, Y)
+        a.record()
+        for _ in range(3):
+            api.fp4q_linear_fwd(xv, wv, Y)
+        b.record()
+        torch.cuda.synchronize()
+        f_us = a.elapsed_time(b) / 3 * 1e3
+        variants[tag] = {"quantize_only_us": round(v_us, 2),
+                         "quantize_only_GB/s": round(v_bytes / (v_us * 1e-6) / 1e9, 1),
+                         "gemm_fwd_us": round(f_us, 1),
+                         "gemm_fwd_TFLOP/s": round(2.0 * M * N * K / (f_us * 1e-6) / 1e12, 1)}
+        del xv, wv, g
+        log(args, f"variant {tag}: quantize-only {v_us:.2f} us, fwd GEMM {f_us:.1f} us")
+    del Xrot
 
     # traffic from committed rocprofv3 counters, valid only for this source
     traffic = None
@@ -276,6 +312,7 @@ def main():
                                        "toward-zero slice additions, 1/1024 snap)",
                                "us": round(probe_us, 1), "TFLOP/s": round(probe_tflops, 1),
                                "frac_bf16_peak": round(probe_tflops / BF16_PEAK_TFLOPS, 4)},
+            "variants": variants,
         },
     }
     print(json.dumps(out), flush=True)

@@ -54,24 +54,30 @@ constexpr int kThreads = 256;
 constexpr int kChunks = BK / 8;              // 16-byte chunks per LDS row
 constexpr int kGroupM = 8;                   // M-tiles per scheduling group
 
-// Codes and scales of one 64-element row segment (4 blocks of 16).
+// Codes and scales of one 64-element row segment (4 blocks of 16, or 2 of
+// 32). The scale bytes are kept as loaded (s0: the first two, s1: the next
+// two, unused for blocks of 32) and picked apart only when decoded, so no
+// arithmetic waits on the loads where they are issued.
 struct RowSeg {
   uint4 c0, c1;    // 32 bytes of codes
-  uint32_t s;      // 4 scale bytes, block j in bits 8j+7:8j
+  uint32_t s0, s1;
 };
 
-// Scale bytes of the four 16-element blocks of a 64-element segment: one
-// byte each for blocks of 16; for blocks of 32 each of the segment's two
-// scale bytes is repeated for its two halves, so consumers index by block
-// of 16 either way.
-__device__ __forceinline__ uint32_t widen32(uint32_t two) {
-  const uint32_t lo = two & 0xFFu, hi = (two >> 8) & 0xFFu;
-  return lo | (lo << 8) | (hi << 16) | (hi << 24);
+// Scale code of the 16-element block j (0..3) of a segment. kFmt false:
+// blocks of 16 only, and s0 holds all four scale bytes.
+template <bool kFmt>
+__device__ __forceinline__ uint32_t seg_scale(const RowSeg& g, int j, bool blk32) {
+  if (!kFmt) return (g.s0 >> (8 * j)) & 0xFFu;
+  const uint32_t w = (blk32 || j < 2) ? g.s0 : g.s1;
+  return (w >> (blk32 ? 8 * (j >> 1) : 8 * (j & 1))) & 0xFFu;
 }
 
 // K % 64 == 0: a whole segment is in bounds; rows past the end are clamped
 // to the last row (their products only reach outputs that are not stored),
-// so the load is branch-free. blk32: blocks of 32 (else 16).
+// so the load is branch-free. blk32: blocks of 32 (else 16); the second
+// 16-bit scale load repeats the first for blocks of 32, so it stays inside
+// the row.
+template <bool kFmt>
 __device__ __forceinline__ RowSeg load_seg_full(const uint8_t* __restrict__ codes,
                                                 const uint8_t* __restrict__ scales, int64_t rows,
                                                 int64_t K, int tile_shift, bool blk32, int64_t r,
@@ -81,18 +87,21 @@ __device__ __forceinline__ RowSeg load_seg_full(const uint8_t* __restrict__ code
   RowSeg g;
   g.c0 = *reinterpret_cast<const uint4*>(cp);
   g.c1 = *reinterpret_cast<const uint4*>(cp + 16);
-  if (blk32) {
-    const uint8_t* sp = scales + (r >> tile_shift) * (K / 32) + k0 / 32;
-    g.s = widen32(*reinterpret_cast<const uint16_t*>(sp));
-  } else {
-    const uint8_t* sp = scales + (r >> tile_shift) * (K / 16) + k0 / 16;
-    g.s = *reinterpret_cast<const uint32_t*>(sp);
+  if (!kFmt) {
+    g.s0 = *reinterpret_cast<const uint32_t*>(scales + (r >> tile_shift) * (K / 16) + k0 / 16);
+    g.s1 = 0u;
+    return g;
   }
+  const int sh = blk32 ? 5 : 4;
+  const uint8_t* sp = scales + (r >> tile_shift) * (K >> sh) + (k0 >> sh);
+  g.s0 = *reinterpret_cast<const uint16_t*>(sp);
+  g.s1 = *reinterpret_cast<const uint16_t*>(blk32 ? sp : sp + 2);
   return g;
 }
 
 // General K (a multiple of the block size): blocks at or beyond K read as
 // zero codes.
+template <bool kFmt>
 __device__ __forceinline__ RowSeg load_seg_tail(const uint8_t* __restrict__ codes,
                                                 const uint8_t* __restrict__ scales, int64_t rows,
                                                 int64_t K, int tile_shift, bool blk32, int64_t r,
@@ -102,31 +111,40 @@ __device__ __forceinline__ RowSeg load_seg_tail(const uint8_t* __restrict__ code
   const uint8_t* cp = codes + r * (K / 2);
   const uint8_t* sp = scales + (r >> tile_shift) * (K / bl);
   uint2 b[4];
-  uint32_t s = 0u;
+  uint32_t sb[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int64_t kb = k0 + 16 * j;
     if (kb < K) {
       b[j] = *reinterpret_cast<const uint2*>(cp + kb / 2);
-      s |= (uint32_t)sp[kb / bl] << (8 * j);
+      sb[j] = sp[kb / bl];
     } else {
       b[j] = make_uint2(0u, 0u);
+      sb[j] = 0u;
     }
   }
   RowSeg g;
   g.c0 = make_uint4(b[0].x, b[0].y, b[1].x, b[1].y);
   g.c1 = make_uint4(b[2].x, b[2].y, b[3].x, b[3].y);
-  g.s = s;
+  // same packing as the full path: for blocks of 32, s0 holds the two
+  // block codes (blocks 0-1 share code 0, blocks 2-3 code 1)
+  if (!kFmt) {
+    g.s0 = sb[0] | (sb[1] << 8) | (sb[2] << 16) | (sb[3] << 24);
+    g.s1 = 0u;
+    return g;
+  }
+  g.s0 = blk32 ? (sb[0] | (sb[2] << 8)) : (sb[0] | (sb[1] << 8));
+  g.s1 = sb[2] | (sb[3] << 8);
   return g;
 }
 
-template <bool kFullK>
+template <bool kFullK, bool kFmt>
 __device__ __forceinline__ RowSeg load_seg(const uint8_t* __restrict__ codes,
                                            const uint8_t* __restrict__ scales, int64_t rows,
                                            int64_t K, int tile_shift, bool blk32, int64_t r,
                                            int64_t k0) {
-  return kFullK ? load_seg_full(codes, scales, rows, K, tile_shift, blk32, r, k0)
-                : load_seg_tail(codes, scales, rows, K, tile_shift, blk32, r, k0);
+  return kFullK ? load_seg_full<kFmt>(codes, scales, rows, K, tile_shift, blk32, r, k0)
+                : load_seg_tail<kFmt>(codes, scales, rows, K, tile_shift, blk32, r, k0);
 }
 
 // 8 codes (one 32-bit word, element e in bits 4e+3:4e) of a block with
@@ -176,14 +194,17 @@ constexpr int row_pitch() { return kSwz == 2 ? kChunks + 1 : kChunks; }
 // to round-toward-zero around those additions only); the epilogue
 // optionally snaps the sum to multiples of 2^-snap_log2 (ties to even)
 // before applying alpha.
-template <int kBM, int kBN, bool kFullK, bool kF32Out, int kWavesM, int kWavesN, int kSwz, bool kProbe>
+template <int kBM, int kBN, bool kFullK, bool kF32Out, int kWavesM, int kWavesN, int kSwz, bool kProbe,
+          bool kFmt>
 __global__ __launch_bounds__(64 * kWavesM * kWavesN) void gemm_kernel(
     const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales, int a_shift,
     const float* __restrict__ a_S, const uint8_t* __restrict__ b_codes,
     const uint8_t* __restrict__ b_scales, int b_shift, const float* __restrict__ b_S, int64_t M,
     int64_t N, int64_t K, int tiles_m, int tiles_n, int snap_log2, int fmt, void* __restrict__ y) {
-  // fmt bits: 0 A blocks of 32, 1 A E4M3 scales, 2 B blocks of 32, 3 B E4M3 scales
-  const bool a_blk32 = fmt & 1, a_e4m3 = fmt & 2, b_blk32 = fmt & 4, b_e4m3 = fmt & 8;
+  // fmt bits: 0 A blocks of 32, 1 A E4M3 scales, 2 B blocks of 32, 3 B E4M3
+  // scales; kFmt false compiles the default (blocks of 16, UE5M3) only
+  const bool a_blk32 = kFmt && (fmt & 1), a_e4m3 = kFmt && (fmt & 2);
+  const bool b_blk32 = kFmt && (fmt & 4), b_e4m3 = kFmt && (fmt & 8);
   constexpr int kT = 64 * kWavesM * kWavesN;  // threads
   constexpr int kTM = kBM / kWavesM;           // wave tile rows
   constexpr int kTN = kBN / kWavesN;           // wave tile cols
@@ -229,8 +250,8 @@ __global__ __launch_bounds__(64 * kWavesM * kWavesN) void gemm_kernel(
 #pragma unroll
     for (int i = 0; i < kRows; ++i) {
       const int q = tid + i * kT;
-      g[i] = q < kBM ? load_seg<kFullK>(a_codes, a_scales, M, K, a_shift, a_blk32, m0 + q, k0)
-                    : load_seg<kFullK>(b_codes, b_scales, N, K, b_shift, b_blk32, n0 + (q - kBM), k0);
+      g[i] = q < kBM ? load_seg<kFullK, kFmt>(a_codes, a_scales, M, K, a_shift, a_blk32, m0 + q, k0)
+                    : load_seg<kFullK, kFmt>(b_codes, b_scales, N, K, b_shift, b_blk32, n0 + (q - kBM), k0);
     }
   };
   // one decode8 piece p (0 .. kPieces-1) of block s into buffer `buf`
@@ -238,7 +259,8 @@ __global__ __launch_bounds__(64 * kWavesM * kWavesN) void gemm_kernel(
     const int i = p >> 1;
     const int q = tid + i * kT;
     const int c = 2 * s + (p & 1);
-    const float dec = scale_value((g[i].s >> (8 * s)) & 0xFFu, q < kBM ? a_e4m3 : b_e4m3);
+    const bool is_a = q < kBM;
+    const float dec = scale_value(seg_scale<kFmt>(g[i], s, is_a ? a_blk32 : b_blk32), is_a ? a_e4m3 : b_e4m3);
     buf[slot<kSwz>(q, c)] = decode8(seg_word(g[i], c), dec);
   };
 
@@ -414,31 +436,28 @@ __global__ __launch_bounds__(64 * kWavesM * kWavesN) void gemm_kernel(
 
 namespace {
 
-template <int kBM, int kBN, int kWM, int kWN, int kSW, bool kProbe>
-hipError_t launch_tiled(const QOperand& a, const QOperand& b, void* y, int y_es, int snap_log2,
-                        hipStream_t s) {
+template <int kBM, int kBN, int kWM, int kWN, int kSW, bool kProbe, bool kFmt>
+hipError_t launch_kernel(const QOperand& a, const QOperand& b, void* y, int y_es, int snap_log2,
+                         int fmt, hipStream_t s) {
   const int64_t M = a.rows, N = b.rows, K = a.cols;
-  if (M == 0 || N == 0) return hipSuccess;
   const int tiles_m = (int)((M + kBM - 1) / kBM);
   const int tiles_n = (int)((N + kBN - 1) / kBN);
   const bool full_k = K % BK == 0;
   const size_t lds_bytes = 2 * (kBM + kBN) * (kSW == 2 ? kChunks + 1 : kChunks) * sizeof(uint4);
   const void* fn;
   if (full_k)
-    fn = y_es == 4 ? (const void*)gemm_kernel<kBM, kBN, true, true, kWM, kWN, kSW, kProbe>
-                   : (const void*)gemm_kernel<kBM, kBN, true, false, kWM, kWN, kSW, kProbe>;
+    fn = y_es == 4 ? (const void*)gemm_kernel<kBM, kBN, true, true, kWM, kWN, kSW, kProbe, kFmt>
+                   : (const void*)gemm_kernel<kBM, kBN, true, false, kWM, kWN, kSW, kProbe, kFmt>;
   else
-    fn = y_es == 4 ? (const void*)gemm_kernel<kBM, kBN, false, true, kWM, kWN, kSW, kProbe>
-                   : (const void*)gemm_kernel<kBM, kBN, false, false, kWM, kWN, kSW, kProbe>;
+    fn = y_es == 4 ? (const void*)gemm_kernel<kBM, kBN, false, true, kWM, kWN, kSW, kProbe, kFmt>
+                   : (const void*)gemm_kernel<kBM, kBN, false, false, kWM, kWN, kSW, kProbe, kFmt>;
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);
   if (e != hipSuccess) return e;
   const dim3 grid((uint32_t)(tiles_m * tiles_n)), block(64 * kWM * kWN);
   const int a_shift = a.tile ? (a.block == 32 ? 5 : 4) : 0;
   const int b_shift = b.tile ? (b.block == 32 ? 5 : 4) : 0;
-  const int fmt = (a.block == 32 ? 1 : 0) | (a.scale_fmt ? 2 : 0) | (b.block == 32 ? 4 : 0) |
-                  (b.scale_fmt ? 8 : 0);
 #define FP4Q_GEMM(FK, F32)                                                                     \
-  hipLaunchKernelGGL((gemm_kernel<kBM, kBN, FK, F32, kWM, kWN, kSW, kProbe>), grid, block,      \
+  hipLaunchKernelGGL((gemm_kernel<kBM, kBN, FK, F32, kWM, kWN, kSW, kProbe, kFmt>), grid, block, \
                      lds_bytes, s, a.codes, a.scales, a_shift, a.enc_scale, b.codes, b.scales,    \
                      b_shift, b.enc_scale, M, N, K, tiles_m, tiles_n, snap_log2, fmt, y)
   if (full_k) {
@@ -450,6 +469,18 @@ hipError_t launch_tiled(const QOperand& a, const QOperand& b, void* y, int y_es,
   }
 #undef FP4Q_GEMM
   return hipGetLastError();
+}
+
+// Operands in the default format (blocks of 16, UE5M3) take kernels
+// compiled for it; any other combination takes the format-generic ones.
+template <int kBM, int kBN, int kWM, int kWN, int kSW, bool kProbe>
+hipError_t launch_tiled(const QOperand& a, const QOperand& b, void* y, int y_es, int snap_log2,
+                        hipStream_t s) {
+  if (a.rows == 0 || b.rows == 0) return hipSuccess;
+  const int fmt = (a.block == 32 ? 1 : 0) | (a.scale_fmt ? 2 : 0) | (b.block == 32 ? 4 : 0) |
+                  (b.scale_fmt ? 8 : 0);
+  if (fmt == 0) return launch_kernel<kBM, kBN, kWM, kWN, kSW, kProbe, false>(a, b, y, y_es, snap_log2, 0, s);
+  return launch_kernel<kBM, kBN, kWM, kWN, kSW, kProbe, true>(a, b, y, y_es, snap_log2, fmt, s);
 }
 
 }  // namespace

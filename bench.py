@@ -178,6 +178,32 @@ def main():
     }
     codec_gbs = {k: codec_bytes[k] * args.steps / (fam_us[k] * 1e-6) / 1e9 for k in codec_bytes}
 
+    # the FP4Linear module (autograd over the same C ABI) on the same shape:
+    # steps 1..steps of its sample-and-hold schedule (D = 50), so no refresh
+    from fp4_block_scaled_fp4q_amd.recipe import Fp4Recipe, FP4Linear
+    layer = FP4Linear(K, N, Fp4Recipe(refresh_period=50), device=dev)
+    with torch.no_grad():
+        layer.weight.copy_(W.float())
+    xin = X.detach().clone().requires_grad_(True)
+
+    def module_step():
+        xin.grad = None
+        layer.weight.grad = None
+        layer(xin).backward(dY)
+
+    module_step()  # step 0: the refresh step
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(args.steps):
+        module_step()
+    b.record()
+    torch.cuda.synchronize()
+    module_ms = a.elapsed_time(b) / args.steps
+    module_tflops = 3 * 2.0 * M * N * K / (module_ms * 1e-3) / 1e12
+    log(args, f"FP4Linear fwd+bwd (held amax): {module_ms:.3f} ms/step, {module_tflops:.1f} TFLOP/s")
+    del layer, xin
+
     # the probe-matched accumulation mode on the forward GEMM (same operands)
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     api.fp4q_linear_probe(xq, wq, Y, 10)
@@ -313,6 +339,10 @@ def main():
                                "us": round(probe_us, 1), "TFLOP/s": round(probe_tflops, 1),
                                "frac_bf16_peak": round(probe_tflops / BF16_PEAK_TFLOPS, 4)},
             "variants": variants,
+            "fp4linear_step": {"what": "FP4Linear module fwd+bwd through torch autograd on the same "
+                                       "shapes, held-amax steps of a D = 50 schedule (no amax "
+                                       "kernels), fp32 master weight quantized directly",
+                               "ms_per_step": round(module_ms, 4), "TFLOP/s": round(module_tflops, 1)},
         },
     }
     print(json.dumps(out), flush=True)

@@ -63,6 +63,17 @@ struct RowSeg {
   uint32_t s0, s1;
 };
 
+// Output tile of grouped position t: kGroupM M-tiles per group, N-tiles
+// column by column inside a group.
+__device__ __forceinline__ void tile_coords(int t, int tiles_m, int tiles_n, int* tm, int* tn) {
+  const int group = t / (kGroupM * tiles_n);
+  const int first_m = group * kGroupM;
+  const int gm = min(tiles_m - first_m, kGroupM);
+  const int in_group = t - group * kGroupM * tiles_n;
+  *tm = first_m + in_group % gm;
+  *tn = in_group / gm;
+}
+
 // Scale code of the 16-element block j (0..3) of a segment. kFmt false:
 // blocks of 16 only, and s0 holds all four scale bytes.
 template <bool kFmt>
@@ -200,7 +211,8 @@ __global__ __launch_bounds__(64 * kWavesM * kWavesN) void gemm_kernel(
     const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales, int a_shift,
     const float* __restrict__ a_S, const uint8_t* __restrict__ b_codes,
     const uint8_t* __restrict__ b_scales, int b_shift, const float* __restrict__ b_S, int64_t M,
-    int64_t N, int64_t K, int tiles_m, int tiles_n, int snap_log2, int fmt, void* __restrict__ y) {
+    int64_t N, int64_t K, int tiles_m, int tiles_n, int snap_log2, int fmt, int split_local,
+    void* __restrict__ y) {
   // fmt bits: 0 A blocks of 32, 1 A E4M3 scales, 2 B blocks of 32, 3 B E4M3
   // scales; kFmt false compiles the default (blocks of 16, UE5M3) only
   const bool a_blk32 = kFmt && (fmt & 1), a_e4m3 = kFmt && (fmt & 2);
@@ -220,21 +232,26 @@ __global__ __launch_bounds__(64 * kWavesM * kWavesN) void gemm_kernel(
 
   // ---- XCD-aware tile order: hardware dispatch sends workgroup L to XCD
   // L % 8; give each XCD a contiguous range of the grouped tile order.
+  // Split tail (split_local >= 0, fp32 output, tile count a multiple of 8):
+  // each XCD's tiles from split_local on are run as two workgroups over the
+  // two halves of K, so the last round of tiles fills the chip; they add
+  // their partial results into an output zeroed beforehand.
   const int ntiles = tiles_m * tiles_n;
   const int L = blockIdx.x;
   const int per_xcd = (ntiles + 7) / 8;
   const int xcd = L % 8;
   const int local = L / 8;
-  const int full_xcds = ntiles % 8 ? ntiles % 8 : 8;  // XCDs that receive per_xcd tiles
-  const int t = xcd < full_xcds ? xcd * per_xcd + local
-                                : full_xcds * per_xcd + (xcd - full_xcds) * (per_xcd - 1) + local;
-  // grouped order: kGroupM M-tiles per group, N-tiles column by column
-  const int group = t / (kGroupM * tiles_n);
-  const int first_m = group * kGroupM;
-  const int gm = min(tiles_m - first_m, kGroupM);
-  const int in_group = t - group * kGroupM * tiles_n;
-  const int tm = first_m + in_group % gm;
-  const int tn = in_group / gm;
+  int t, half = -1;
+  if (split_local >= 0 && local >= split_local) {
+    t = xcd * per_xcd + split_local + (local - split_local) / 2;
+    half = (local - split_local) & 1;
+  } else {
+    const int full_xcds = ntiles % 8 ? ntiles % 8 : 8;  // XCDs that receive per_xcd tiles
+    t = xcd < full_xcds ? xcd * per_xcd + local
+                        : full_xcds * per_xcd + (xcd - full_xcds) * (per_xcd - 1) + local;
+  }
+  int tm, tn;
+  tile_coords(t, tiles_m, tiles_n, &tm, &tn);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -279,15 +296,18 @@ __global__ __launch_bounds__(64 * kWavesM * kWavesN) void gemm_kernel(
 #pragma unroll
       for (int e = 0; e < 16; ++e) tot[i][j][e] = 0.0f;
 
-  const int nk = (int)((K + BK - 1) / BK);
+  const int nk_all = (int)((K + BK - 1) / BK);
+  // k tiles [k_begin, nk) of this workgroup: all, or one half for a split tile
+  const int k_begin = half == 1 ? nk_all / 2 : 0;
+  const int nk = half == 0 ? nk_all / 2 : nk_all;
   RowSeg g[kRows];  // codes of tile kt + 1, decoded during iteration kt
-  if (nk > 0) {
-    load_rows(g, 0);
+  if (nk > k_begin) {
+    load_rows(g, (int64_t)k_begin * BK);
 #pragma unroll
     for (int s = 0; s < 4; ++s)
 #pragma unroll
       for (int p = 0; p < kPieces; ++p) decode_piece(lds, g, s, p);
-    load_rows(g, (int64_t)min(1, nk - 1) * BK);
+    load_rows(g, (int64_t)min(k_begin + 1, nk - 1) * BK);
     __syncthreads();
   }
 
@@ -303,10 +323,10 @@ __global__ __launch_bounds__(64 * kWavesM * kWavesN) void gemm_kernel(
     for (int j = 0; j < kFN; ++j) bfr[j] = __builtin_bit_cast(bf16x8, buf[slot<kSwz>(brow0 + 32 * j, ch)]);
   };
 
-  for (int kt = 0; kt < nk; ++kt) {
+  for (int kt = k_begin; kt < nk; ++kt) {
     constexpr int kBuf = (kBM + kBN) * row_pitch<kSwz>();
-    const uint4* cur_buf = lds + (kt & 1) * kBuf;
-    uint4* next_buf = lds + ((kt + 1) & 1) * kBuf;
+    const uint4* cur_buf = lds + ((kt - k_begin) & 1) * kBuf;
+    uint4* next_buf = lds + ((kt - k_begin + 1) & 1) * kBuf;
     // codes of tile kt + 2 (the last tile again near the end: harmless)
     RowSeg ng[kRows];
     load_rows(ng, (int64_t)min(kt + 2, nk - 1) * BK);
@@ -374,6 +394,23 @@ __global__ __launch_bounds__(64 * kWavesM * kWavesN) void gemm_kernel(
   const float alpha = (float)alpha_d;
   const bool alpha_normal = alpha >= 1.17549435e-38f && alpha <= 3.40282347e+38f;
   constexpr int es = kF32Out ? 4 : 2;
+  if (kF32Out && half >= 0) {
+    // one half of a split tile: add into the zeroed output (two additions
+    // onto zero give the same sum in either order)
+#pragma unroll
+    for (int i = 0; i < kFM; ++i)
+#pragma unroll
+      for (int j = 0; j < kFN; ++j) {
+        const int64_t c = n0 + wn * kTN + j * 32 + (lane & 31);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int64_t r = m0 + wm * kTM + i * 32 + 8 * (e >> 2) + 4 * hi + (e & 3);
+          const float v = alpha_normal ? acc[i][j][e] * alpha : (float)((double)acc[i][j][e] * alpha_d);
+          if (r < M && c < N) unsafeAtomicAdd(static_cast<float*>(y) + r * N + c, v);
+        }
+      }
+    return;
+  }
   const bool full_tile = m0 + kBM <= M && n0 + kBN <= N;
   if (full_tile && alpha_normal && N * es * kBM < 0xFFFFFFFFll) {
     char* tile_base = static_cast<char*>(y) + (m0 * N + n0) * es;
@@ -418,6 +455,23 @@ __global__ __launch_bounds__(64 * kWavesM * kWavesN) void gemm_kernel(
     }
 }
 
+// Zeroes the fp32 output tiles that split workgroups add into: workgroup j
+// takes split tile j (nsplit of them per XCD range), with consecutive
+// threads on consecutive columns.
+__global__ __launch_bounds__(256) void zero_split_tiles(float* __restrict__ y, int64_t M, int64_t N,
+                                                        int tiles_m, int tiles_n, int per_xcd,
+                                                        int split_local, int nsplit, int bm, int bn) {
+  const int xcd = blockIdx.x / nsplit;
+  const int t = xcd * per_xcd + split_local + (int)(blockIdx.x % nsplit);
+  int tm, tn;
+  tile_coords(t, tiles_m, tiles_n, &tm, &tn);
+  const int64_t m0 = (int64_t)tm * bm, n0 = (int64_t)tn * bn;
+  for (int i = threadIdx.x; i < bm * bn; i += 256) {
+    const int64_t r = m0 + i / bn, c = n0 + i % bn;
+    if (r < M && c < N) y[r * N + c] = 0.0f;
+  }
+}
+
 }  // namespace
 
 // Kernel configuration, chosen at build time: 2 x 4 waves (two per SIMD, so
@@ -436,6 +490,16 @@ __global__ __launch_bounds__(64 * kWavesM * kWavesN) void gemm_kernel(
 
 namespace {
 
+// Workgroups of the default kernel that run at once on the current device:
+// one per compute unit (its LDS use allows one per CU).
+int concurrent_workgroups() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    return 256;
+  return cus;
+}
+
 template <int kBM, int kBN, int kWM, int kWN, int kSW, bool kProbe, bool kFmt>
 hipError_t launch_kernel(const QOperand& a, const QOperand& b, void* y, int y_es, int snap_log2,
                          int fmt, hipStream_t s) {
@@ -453,13 +517,32 @@ hipError_t launch_kernel(const QOperand& a, const QOperand& b, void* y, int y_es
                    : (const void*)gemm_kernel<kBM, kBN, false, false, kWM, kWN, kSW, kProbe, kFmt>;
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);
   if (e != hipSuccess) return e;
-  const dim3 grid((uint32_t)(tiles_m * tiles_n)), block(64 * kWM * kWN);
+  // split tail: when the tiles fill the last round of workgroups at most
+  // half way, run each of those tiles as two K halves (fp32 output only)
+  const int ntiles = tiles_m * tiles_n;
+  const int nk = (int)((K + BK - 1) / BK);
+  const int per_xcd = (ntiles + 7) / 8;
+  int split_local = -1;
+  const int cwg = (!kProbe && y_es == 4) ? concurrent_workgroups() : 1;
+  const int rem = ntiles % cwg;
+#ifndef FP4Q_NO_SPLIT_TAIL
+  if (!kProbe && y_es == 4 && ntiles % 8 == 0 && rem > 0 && rem % 8 == 0 && 2 * rem <= cwg && nk >= 2)
+    split_local = per_xcd - rem / 8;
+#endif
+  const int nwg = split_local < 0 ? ntiles : 8 * (split_local + 2 * (per_xcd - split_local));
+  if (split_local >= 0) {
+    const int nsplit = per_xcd - split_local;
+    hipLaunchKernelGGL(zero_split_tiles, dim3((uint32_t)(8 * nsplit)), dim3(256), 0, s,
+                       static_cast<float*>(y), M, N, tiles_m, tiles_n, per_xcd, split_local, nsplit,
+                       kBM, kBN);
+  }
+  const dim3 grid((uint32_t)nwg), block(64 * kWM * kWN);
   const int a_shift = a.tile ? (a.block == 32 ? 5 : 4) : 0;
   const int b_shift = b.tile ? (b.block == 32 ? 5 : 4) : 0;
 #define FP4Q_GEMM(FK, F32)                                                                     \
   hipLaunchKernelGGL((gemm_kernel<kBM, kBN, FK, F32, kWM, kWN, kSW, kProbe, kFmt>), grid, block, \
                      lds_bytes, s, a.codes, a.scales, a_shift, a.enc_scale, b.codes, b.scales,    \
-                     b_shift, b.enc_scale, M, N, K, tiles_m, tiles_n, snap_log2, fmt, y)
+                     b_shift, b.enc_scale, M, N, K, tiles_m, tiles_n, snap_log2, fmt, split_local, y)
   if (full_k) {
     if (y_es == 4) FP4Q_GEMM(true, true);
     else FP4Q_GEMM(true, false);

@@ -113,3 +113,24 @@ def test_gemm_deterministic_and_launch_independent():
     y3 = torch.empty((128, 384), device=DEV)
     api.fp4q_linear_fwd(sub, qb, y3)
     assert torch.equal(y3, y1[128:256])
+
+
+@pytest.mark.parametrize("M,N,K", [(512, 1024, 1024), (500, 1000, 1040), (2048, 1024, 512)])
+def test_split_tail_fp32_gemm(M, N, K):
+    # fp32 outputs whose tile count leaves the last round of workgroups at
+    # most half full run those tiles as two K halves added into a zeroed
+    # output (here: 8, 8 and 32 tiles of 256 x 256); results stay within the
+    # GEMM bound and are identical from run to run
+    rng = np.random.default_rng(M + N + K)
+    a = torch.from_numpy(rng.standard_normal((M, K)).astype(np.float32))
+    b = torch.from_numpy((0.02 * rng.standard_normal((N, K))).astype(np.float32))
+    ga, oa = quant_both(a, float(np.abs(a.numpy()).max()), "row16")
+    gb, ob = quant_both(b, float(np.abs(b.numpy()).max()), "row16")
+    y1 = torch.full((M, N), float("nan"), dtype=torch.float32, device=DEV)
+    y2 = torch.full((M, N), float("nan"), dtype=torch.float32, device=DEV)
+    api.fp4q_linear_wgrad(ga["q"], gb["q"], y1)
+    api.fp4q_linear_wgrad(ga["q"], gb["q"], y2)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
+    ref = oracle.gemm(oa.q, ob.q)
+    assert rel_fro(y1.cpu().numpy(), round_out(ref, torch.float32)) <= GEMM_TOL

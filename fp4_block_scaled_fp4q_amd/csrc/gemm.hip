@@ -456,8 +456,8 @@ __global__ __launch_bounds__(64 * kWavesM * kWavesN) void gemm_kernel(
 }
 
 // Zeroes the fp32 output tiles that split workgroups add into: workgroup j
-// takes split tile j (nsplit of them per XCD range), with consecutive
-// threads on consecutive columns.
+// takes split tile j (nsplit of them per XCD range); each wave writes whole
+// tile rows, 16 bytes per lane (y is 16-byte aligned and N % 4 == 0).
 __global__ __launch_bounds__(256) void zero_split_tiles(float* __restrict__ y, int64_t M, int64_t N,
                                                         int tiles_m, int tiles_n, int per_xcd,
                                                         int split_local, int nsplit, int bm, int bn) {
@@ -465,10 +465,12 @@ __global__ __launch_bounds__(256) void zero_split_tiles(float* __restrict__ y, i
   const int t = xcd * per_xcd + split_local + (int)(blockIdx.x % nsplit);
   int tm, tn;
   tile_coords(t, tiles_m, tiles_n, &tm, &tn);
-  const int64_t m0 = (int64_t)tm * bm, n0 = (int64_t)tn * bn;
-  for (int i = threadIdx.x; i < bm * bn; i += 256) {
-    const int64_t r = m0 + i / bn, c = n0 + i % bn;
-    if (r < M && c < N) y[r * N + c] = 0.0f;
+  const int64_t m0 = (int64_t)tm * bm;
+  const int64_t c = (int64_t)tn * bn + 4 * (threadIdx.x & 63);
+  const bool cv = c < N && 4 * (int)(threadIdx.x & 63) < bn;
+  for (int r = threadIdx.x >> 6; r < bm; r += 4) {
+    if (cv && m0 + r < M)
+      *reinterpret_cast<float4*>(y + (m0 + r) * N + c) = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
   }
 }
 
@@ -526,7 +528,8 @@ hipError_t launch_kernel(const QOperand& a, const QOperand& b, void* y, int y_es
   const int cwg = (!kProbe && y_es == 4) ? concurrent_workgroups() : 1;
   const int rem = ntiles % cwg;
 #ifndef FP4Q_NO_SPLIT_TAIL
-  if (!kProbe && y_es == 4 && ntiles % 8 == 0 && rem > 0 && rem % 8 == 0 && 2 * rem <= cwg && nk >= 2)
+  if (!kProbe && y_es == 4 && ntiles % 8 == 0 && rem > 0 && rem % 8 == 0 && 2 * rem <= cwg && nk >= 2 &&
+      reinterpret_cast<uintptr_t>(y) % 16 == 0 && N % 4 == 0 && kBN <= 256)
     split_local = per_xcd - rem / 8;
 #endif
   const int nwg = split_local < 0 ? ntiles : 8 * (split_local + 2 * (per_xcd - split_local));

@@ -134,3 +134,9 @@ def test_split_tail_fp32_gemm(M, N, K):
     assert torch.equal(y1, y2)
     ref = oracle.gemm(oa.q, ob.q)
     assert rel_fro(y1.cpu().numpy(), round_out(ref, torch.float32)) <= GEMM_TOL
+    # an output that is not 16-byte aligned takes the unsplit path
+    buf = torch.full((M * N + 1,), float("nan"), dtype=torch.float32, device=DEV)
+    y3 = buf[1:].view(M, N)
+    api.fp4q_linear_wgrad(ga["q"], gb["q"], y3)
+    torch.cuda.synchronize()
+    assert rel_fro(y3.cpu().numpy(), round_out(ref, torch.float32)) <= GEMM_TOL

@@ -15,13 +15,23 @@ constexpr int64_t kMaxGridX = 0x7FFFFFFF / 256;  // workgroups of 256 threads
 
 int elem_size(int dt) { return dt == FP4Q_F32 ? 4 : (dt == FP4Q_BF16 ? 2 : 0); }
 
+// Sizes beyond any device memory are rejected up front, so the launch
+// arithmetic below (products of two sizes, grid counts) cannot overflow:
+// each dimension at most 2^40, and at most 2^44 elements.
+constexpr int64_t kMaxDim = int64_t(1) << 40;
+constexpr int64_t kMaxElems = int64_t(1) << 44;
+bool dims_ok(int64_t a, int64_t b) {
+  if (a < 0 || b < 0 || a > kMaxDim || b > kMaxDim) return false;
+  return a == 0 || b <= kMaxElems / a;
+}
+
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 fp4q_status from_hip(hipError_t e) { return e == hipSuccess ? FP4Q_OK : FP4Q_E_HIP; }
 
 fp4q_status check_operand(const fp4q_qtensor* q) {
   if (!q) return FP4Q_E_NULL;
-  if (q->rows < 0 || q->cols < 0) return FP4Q_E_SHAPE;
+  if (!dims_ok(q->rows, q->cols)) return FP4Q_E_SHAPE;
   if (q->layout != FP4Q_ROW16 && q->layout != FP4Q_TILE16x16) return FP4Q_E_ARG;
   if (q->block != 16 && q->block != 32) return FP4Q_E_ARG;
   if (q->scale_fmt != FP4Q_UE5M3 && q->scale_fmt != FP4Q_E4M3) return FP4Q_E_ARG;
@@ -56,7 +66,8 @@ fp4q_status gemm(const fp4q_qtensor* a, const fp4q_qtensor* b, void* y, fp4q_dty
   if (!es) return FP4Q_E_DTYPE;
   if (a->cols != b->cols) return FP4Q_E_SHAPE;
   if (a->rows > 0 && b->rows > 0 && !y) return FP4Q_E_NULL;
-  if (((a->rows + 127) / 128) * ((b->rows + 127) / 128) > 0x7FFFFFFF / 512) return FP4Q_E_SHAPE;
+  const int64_t tm = (a->rows + 127) / 128, tn = (b->rows + 127) / 128;
+  if (tm > 0 && tn > (0x7FFFFFFF / 512) / tm) return FP4Q_E_SHAPE;
   if (probe)
     return from_hip(fp4q::launch_gemm_probe(to_operand(a), to_operand(b), y, es, snap_log2,
                                             static_cast<hipStream_t>(stream)));
@@ -88,7 +99,7 @@ fp4q_status fp4q_amax(const void* x, fp4q_dtype xt, int64_t rows, int64_t cols, 
   const int es = elem_size(xt);
   if (!es) return FP4Q_E_DTYPE;
   if (!amax_out) return FP4Q_E_NULL;
-  if (rows < 0 || cols < 0 || ld < cols) return FP4Q_E_SHAPE;
+  if (!dims_ok(rows, cols) || !dims_ok(rows, ld) || ld < cols) return FP4Q_E_SHAPE;
   if (rows > 0 && cols > 0) {
     if (!x) return FP4Q_E_NULL;
     if (!aligned(x, 16) || (cols * es) % 16 || (ld * es) % 16) return FP4Q_E_ALIGN;
@@ -116,7 +127,7 @@ fp4q_status fp4q_quantize_fmt(const void* x, fp4q_dtype xt, int64_t rows, int64_
   // ROW with the second orientation also needs whole column blocks
   if (codes_t && layout == FP4Q_ROW16 && rows % block) return FP4Q_E_SHAPE;
   if (!amax_held) return FP4Q_E_NULL;
-  if (rows < 0 || cols < 0 || ld < cols) return FP4Q_E_SHAPE;
+  if (!dims_ok(rows, cols) || !dims_ok(rows, ld) || ld < cols) return FP4Q_E_SHAPE;
   if (layout != FP4Q_COL16 && cols % block) return FP4Q_E_SHAPE;
   if (layout != FP4Q_ROW16 && rows % block) return FP4Q_E_SHAPE;
   if (layout == FP4Q_COL16 && cols % 8) return FP4Q_E_ALIGN;

@@ -133,3 +133,21 @@ def test_format_validation():
     assert qf(rows=48, layout=_lib.COL16) == _lib.E_SHAPE    # COL blocks of 32
     assert qf(rows=48, layout=_lib.TILE16x16) == _lib.E_SHAPE
     assert qf(rows=48, ct=FAKE, st=FAKE) == _lib.E_SHAPE     # ROW + COL needs rows % 32
+
+
+def test_oversized_grids_are_rejected():
+    # shapes whose launch would exceed the grid limits come back as
+    # FP4Q_E_SHAPE before anything is enqueued (nothing is dereferenced)
+    L = _lib.lib()
+    huge = 1 << 40
+    assert L.fp4q_quantize(FAKE, _lib.BF16, huge, 4096, 4096, FAKE, 448.0, _lib.ROW16, _lib.RNE, 0, 0,
+                           FAKE, FAKE, None, None, None, None, None) == _lib.E_SHAPE
+    assert L.fp4q_quantize(FAKE, _lib.BF16, huge, 4096, 4096, FAKE, 448.0, _lib.TILE16x16, _lib.RNE, 0,
+                           0, FAKE, FAKE, None, None, None, None, None) == _lib.E_SHAPE
+    assert L.fp4q_quantize(FAKE, _lib.BF16, huge, 4096, 4096, FAKE, 448.0, _lib.COL16, _lib.RNE, 0, 0,
+                           FAKE, FAKE, None, None, None, None, None) == _lib.E_SHAPE
+    assert L.fp4q_linear_fwd(q(huge, 64), q(huge, 64), FAKE, _lib.F32, None) == _lib.E_SHAPE
+    assert L.fp4q_dequant(q(huge, 4096), FAKE, _lib.F32, None) == _lib.E_SHAPE
+    # negative sizes
+    assert L.fp4q_amax(FAKE, _lib.BF16, -1, 16, 16, FAKE, None) == _lib.E_SHAPE
+    assert L.fp4q_linear_fwd(q(-16, 64), q(16, 64), FAKE, _lib.F32, None) == _lib.E_SHAPE

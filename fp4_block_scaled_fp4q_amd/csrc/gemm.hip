@@ -4,8 +4,11 @@
 // tensor-scale product applied after accumulation).
 //
 // Each decoded element e2m1 * dec has at most 6 significant bits and lies in
-// [2^-18, 368640], so it is exact in bf16; the contraction runs on bf16 MFMA
-// (v_mfma_f32_32x32x16_bf16) with fp32 accumulation.
+// [2^-18, 368640]. The default accumulation decodes it times 2^-5, which is
+// exact in binary16 (at most 11520, a multiple of 2^-23), and contracts on
+// v_mfma_f32_32x32x16_f16 with fp32 accumulation; alpha absorbs the 2^10.
+// The probe-matched mode decodes to bf16 (exact as well) and contracts on
+// v_mfma_f32_32x32x16_bf16.
 //
 // Design (gfx950):
 //  * A workgroup owns a 256 x 256 output tile; its 8 waves (2 along M x 4
@@ -14,20 +17,23 @@
 //  * K advances in tiles of 64. FP4 codes (0.5 B/element) and one scale byte
 //    per 16 elements are read from global memory two tiles ahead into
 //    registers; every thread decodes one 64-element row of the stacked
-//    [A tile; B tile] to bf16 into LDS, double buffered, in pieces placed
-//    between the MFMAs that consume the other buffer. Decoding once per
-//    workgroup costs (256 + 256) * 64 elements per 256 * 256 * 64 MACs.
-//  * Decode: v_cvt_scalef32_pk_f32_fp4 (scale 1.0) gives two exact E2M1
-//    values in fp32, one multiply each by the block's UE5M3 value (exact),
-//    and v_cvt_pk_bf16_f32 packs the exact products.
+//    [A tile; B tile] into LDS, double buffered, in pieces placed between
+//    the MFMAs that consume the other buffer. Decoding once per workgroup
+//    costs (256 + 256) * 64 elements per 256 * 256 * 64 MACs.
+//  * Decode: v_cvt_scalef32_pk_f16_fp4 (scale 1.0) gives two exact E2M1
+//    values as halves and one packed half multiply by the block's scale pair
+//    forms the products: two instructions per pair of elements. (The bf16
+//    decode of the probe mode takes four: a conversion to fp32, two fp32
+//    multiplies and a packing conversion.)
 //  * LDS rows are 8 chunks of 16 bytes (8 k each) at a 144-byte pitch, so
 //    any 16 consecutive rows fall on distinct banks for the fragment reads
 //    (32 rows, one chunk) and the row-wise decode writes.
 //  * Workgroups are numbered so that consecutive ones on one XCD (hardware
 //    dispatch is round-robin over the 8 XCDs) cover a compact group of tiles,
 //    which keeps their shared A and B rows in that XCD's L2.
-//  * Measured on the FFN shapes (16384 x 14336 x 4096 and its dgrad / wgrad)
-//    this runs at the rate of the vendor bf16 GEMM on plain bf16 operands.
+//  * Under sustained load the chip runs power-limited (its clock drops well
+//    below the nominal 2.4 GHz); the binary16 decode's fewer VALU
+//    instructions measured about 4% faster than the bf16 decode.
 //
 // One kernel serves fwd (A = X, ROW16; B = W, TILE), dgrad (A = dY, ROW16;
 // B = W^T, TILE) and wgrad (A = dY^T, B = X^T, both quantized along tokens):
@@ -42,6 +48,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int BM = 256;   // tile of the default kernel
 constexpr int BN = 256;
@@ -173,6 +181,34 @@ __device__ __forceinline__ uint4 decode8(uint32_t w, float dec) {
                     __builtin_bit_cast(uint32_t, b2), __builtin_bit_cast(uint32_t, b3));
 }
 
+// The same 8 codes -> 8 halves e2m1 * m, with m = (dec 2^-5, dec 2^-5) the
+// block's scale pair from half_scale: v_cvt_scalef32_pk_f16_fp4 (scale 1.0)
+// gives the exact E2M1 values and one packed half multiply per pair forms
+// the products, which are exact in binary16 (see half_scale).
+__device__ __forceinline__ uint4 decode8_h(uint32_t w, f16x2 m) {
+  const f16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0);
+  const f16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1);
+  const f16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2);
+  const f16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3);
+  return make_uint4(__builtin_bit_cast(uint32_t, p0 * m), __builtin_bit_cast(uint32_t, p1 * m),
+                    __builtin_bit_cast(uint32_t, p2 * m), __builtin_bit_cast(uint32_t, p3 * m));
+}
+
+// Scale pair of the binary16 decode: dec 2^-5 in both halves. A UE5M3 code c
+// has the value of the half with bit pattern c << 7, so one packed multiply
+// by 2^-5 (2^3 for E4M3, whose value is the UE5M3 one times 2^8) gives it,
+// exactly: dec 2^-5 lies in [2^-22, 1920] and is a multiple of 2^-24.
+// Every product e2m1 * dec 2^-5 is then exact in binary16 as well: it is at
+// most 6 * 1920 = 11520, and it is an integer of at most 8 bits times a power
+// of two no smaller than 2^-23. The products of two such operands are exact
+// in the MFMA's binary32 arithmetic, so the accumulated sums are the bf16
+// path's sums times 2^-10, and alpha is taken 2^10 times larger.
+__device__ __forceinline__ f16x2 half_scale(uint32_t code, bool e4m3) {
+  const f16x2 v = __builtin_bit_cast(f16x2, (code << 7) | (code << 23));
+  const _Float16 k = e4m3 ? (_Float16)8.0f : (_Float16)0.03125f;
+  return v * f16x2{k, k};
+}
+
 __device__ __forceinline__ uint32_t seg_word(const RowSeg& g, int c) {
   switch (c) {
     case 0: return g.c0.x;
@@ -226,6 +262,9 @@ __global__ __launch_bounds__(64 * kWavesM * kWavesN) void gemm_kernel(
   constexpr int kPieces = 2 * kRows;          // decode8 calls per thread per k16 step
   constexpr int kMfmaPerPiece = kFM * kFN / kPieces;
   static_assert(kFM * kFN % kPieces == 0, "MFMA count must split evenly");
+  // operands decoded to binary16 (times 2^-5) for the default accumulation;
+  // the probe mode keeps bf16
+  constexpr bool kF16 = !kProbe;
 
   // 2 buffers x (A tile + B tile) = 128 KiB
   extern __shared__ uint4 lds[];
@@ -277,8 +316,12 @@ __global__ __launch_bounds__(64 * kWavesM * kWavesN) void gemm_kernel(
     const int q = tid + i * kT;
     const int c = 2 * s + (p & 1);
     const bool is_a = q < kBM;
-    const float dec = scale_value(seg_scale<kFmt>(g[i], s, is_a ? a_blk32 : b_blk32), is_a ? a_e4m3 : b_e4m3);
-    buf[slot<kSwz>(q, c)] = decode8(seg_word(g[i], c), dec);
+    const uint32_t code = seg_scale<kFmt>(g[i], s, is_a ? a_blk32 : b_blk32);
+    const bool e4m3 = is_a ? a_e4m3 : b_e4m3;
+    if constexpr (kF16)
+      buf[slot<kSwz>(q, c)] = decode8_h(seg_word(g[i], c), half_scale(code, e4m3));
+    else
+      buf[slot<kSwz>(q, c)] = decode8(seg_word(g[i], c), scale_value(code, e4m3));
   };
 
   f32x16 acc[kFM][kFN];
@@ -345,8 +388,13 @@ __global__ __launch_bounds__(64 * kWavesM * kWavesN) void gemm_kernel(
         for (int u = 0; u < kMfmaPerPiece; ++u) {
           const int f = p * kMfmaPerPiece + u;
           const int i = f / kFN, j = f % kFN;
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              af[cb][i], bfr[cb][j], (kProbe && s == 0) ? f32x16{} : acc[i][j], 0, 0, 0);
+          if constexpr (kF16)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, af[cb][i]),
+                                                               __builtin_bit_cast(f16x8, bfr[cb][j]),
+                                                               acc[i][j], 0, 0, 0);
+          else
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                af[cb][i], bfr[cb][j], (kProbe && s == 0) ? f32x16{} : acc[i][j], 0, 0, 0);
         }
         decode_piece(next_buf, g, s, p);
         __builtin_amdgcn_sched_barrier(0);
@@ -390,7 +438,7 @@ __global__ __launch_bounds__(64 * kWavesM * kWavesN) void gemm_kernel(
   // epilogue: y = acc * alpha, alpha = 1 / (Sa Sb). Interior tiles (and a
   // normal fp32 alpha) take a branch-free path: a uniform tile base plus
   // 32-bit in-tile offsets, two rows per step.
-  const double alpha_d = 1.0 / ((double)*a_S * (double)*b_S);
+  const double alpha_d = (kF16 ? 1024.0 : 1.0) / ((double)*a_S * (double)*b_S);
   const float alpha = (float)alpha_d;
   const bool alpha_normal = alpha >= 1.17549435e-38f && alpha <= 3.40282347e+38f;
   constexpr int es = kF32Out ? 4 : 2;

@@ -140,3 +140,47 @@ def test_split_tail_fp32_gemm(M, N, K):
     api.fp4q_linear_wgrad(ga["q"], gb["q"], y3)
     torch.cuda.synchronize()
     assert rel_fro(y3.cpu().numpy(), round_out(ref, torch.float32)) <= GEMM_TOL
+
+
+def _coded_operand(rng, rows, cols, code_lo, code_hi, S, tile=False, scale_fmt=api.UE5M3):
+    """Random payload codes and scale codes in [code_lo, code_hi), the same
+    operand for the GPU and the oracle."""
+    codes = rng.integers(0, 256, size=(rows, cols // 2), dtype=np.uint8)
+    scales = rng.integers(code_lo, code_hi, size=(rows // 16 if tile else rows, cols // 16), dtype=np.uint8)
+    g = api.QTensor(torch.from_numpy(codes).to(DEV), torch.from_numpy(scales).to(DEV), dev_scalar(S), rows,
+                    cols, api.TILE16x16 if tile else api.ROW16, scale_fmt=scale_fmt)
+    o = oracle.QTensor(codes, scales, np.float32(S), rows, cols, oracle.TILE16 if tile else oracle.ROW16,
+                       scale_fmt=scale_fmt)
+    return g, o
+
+
+@pytest.mark.parametrize("case", [
+    # (A codes, B codes, scale format): subnormal UE5M3 scales (down to
+    # 2^-17) against mid-range ones; the largest codes (up to 61440) on both
+    # sides; the whole UE5M3 range; the whole E4M3 range (2^-9 .. 448)
+    ((0x01, 0x09), (0x70, 0x80), api.UE5M3),
+    ((0xE8, 0xF8), (0xE8, 0xF8), api.UE5M3),
+    ((0x01, 0xF8), (0x01, 0xF8), api.UE5M3),
+    ((0x01, 0x7F), (0x01, 0x7F), api.E4M3),
+])
+@pytest.mark.parametrize("out", [torch.float32, torch.bfloat16])
+def test_gemm_extreme_scale_codes(case, out):
+    # every decoded value e2m1 * dec, from 2^-18 to 368640, enters the
+    # contraction exactly: an operand decode that lost range or precision
+    # anywhere would show against the exact fp64 contraction
+    (alo, ahi), (blo, bhi), fmt = case
+    rng = np.random.default_rng(alo * 31 + blo + fmt)
+    M, N, K = 300, 272, 1088
+    ga, oa = _coded_operand(rng, M, K, alo, ahi, 0.5, scale_fmt=fmt)
+    gb, ob = _coded_operand(rng, N, K, blo, bhi, 3.0, tile=True, scale_fmt=fmt)
+    y = torch.full((M, N), float("nan"), dtype=out, device=DEV)
+    api.fp4q_linear_fwd(ga, gb, y)
+    torch.cuda.synchronize()
+    ref = oracle.gemm(oa, ob)
+    yf = y.float().cpu().numpy()
+    assert np.isfinite(yf).all()
+    if fmt == api.UE5M3 and alo == 0x01 and ahi == 0x09:
+        # scales with a narrow range: every output is a short exact-product
+        # sum, so fp32 accumulation leaves only a tiny relative error
+        assert rel_fro(yf, round_out(ref, out)) <= (2e-5 if out == torch.float32 else GEMM_TOL)
+    _gemm_check(y, ref)

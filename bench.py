@@ -32,7 +32,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-BF16_PEAK_TFLOPS = 2500.0
+MFMA16_PEAK_TFLOPS = 2500.0  # dense fp16 / bf16 MFMA, MI355X
 METRIC = "FP4-emulated linear TFLOP/s (fwd+dgrad+wgrad) and quantize GB/s, % of roofline"
 
 
@@ -47,6 +47,8 @@ def parse():
                     help="profiling mode: run only this launch of the step (e.g. gemm_fwd, "
                          "quant_x_row16, quantize_only, copy) --reps times and exit")
     ap.add_argument("--reps", type=int, default=5)
+    ap.add_argument("--pack", choices=("k64", "rows"), default="k64",
+                    help="memory packing of the step's quantized operands")
     return ap.parse_args()
 
 
@@ -82,15 +84,15 @@ def main():
     f32 = dict(dtype=torch.float32, device=dev)
     amax = {k: torch.empty(1, **f32) for k in ("X", "W", "dY")}
     S = {k: torch.empty(1, **f32) for k in ("x", "w", "dy")}
-    xq = api.QTensor(torch.empty((M, K // 2), **u8), torch.empty((M, K // 16), **u8), S["x"], M, K, api.ROW16)
-    wq = api.QTensor(torch.empty((N, K // 2), **u8), torch.empty((N // 16, K // 16), **u8), S["w"], N, K,
-                     api.TILE16x16)
-    wqt = api.QTensor(torch.empty((K, N // 2), **u8), torch.empty((K // 16, N // 16), **u8), S["w"], K, N,
-                      api.TILE16x16)
-    dyq = api.QTensor(torch.empty((M, N // 2), **u8), torch.empty((M, N // 16), **u8), S["dy"], M, N, api.ROW16)
-    dyqt = api.QTensor(torch.empty((N, M // 2), **u8), torch.empty((N, M // 16), **u8), S["dy"], N, M,
-                       api.ROW16)
-    xqt = api.QTensor(torch.empty((K, M // 2), **u8), torch.empty((K, M // 16), **u8), S["x"], K, M, api.ROW16)
+    pack = api.PACK_K64 if args.pack == "k64" else api.PACK_ROWS
+
+    def operand(rows, cols, tile, s):
+        codes, scales = api.operand_buffers(rows, cols, tile, 16, pack, dev)
+        return api.QTensor(codes, scales, s, rows, cols, api.TILE16x16 if tile else api.ROW16, 16, api.UE5M3,
+                           pack)
+    xq, xqt = operand(M, K, False, S["x"]), operand(K, M, False, S["x"])
+    wq, wqt = operand(N, K, True, S["w"]), operand(K, N, True, S["w"])
+    dyq, dyqt = operand(M, N, False, S["dy"]), operand(N, M, False, S["dy"])
     Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     dX = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
     dW = torch.empty((N, K), **f32)
@@ -103,14 +105,16 @@ def main():
         ("amax", lambda: api.fp4q_amax(W, amax["W"])),
         ("amax", lambda: api.fp4q_amax(dY, amax["dY"])),
         # X: ROW16 (fwd) and COL16 (wgrad) in one pass
-        ("quant_x_row_col", lambda: api.fp4q_quantize(X, amax["X"], T, api.ROW16, api.RNE, 0, 0,
-                                                      xq.codes, xq.scales, S["x"], xqt.codes, xqt.scales)),
-        ("quant_w_tile", lambda: api.fp4q_quantize(W, amax["W"], T, api.TILE16x16, api.RNE, 0, 0,
-                                                   wq.codes, wq.scales, S["w"], wqt.codes, wqt.scales)),
+        ("quant_x_row_col", lambda: api.fp4q_quantize_fmt(X, amax["X"], T, api.ROW16, 16, api.UE5M3, pack,
+                                                          api.RNE, 0, 0, xq.codes, xq.scales, S["x"],
+                                                          xqt.codes, xqt.scales)),
+        ("quant_w_tile", lambda: api.fp4q_quantize_fmt(W, amax["W"], T, api.TILE16x16, 16, api.UE5M3, pack,
+                                                       api.RNE, 0, 0, wq.codes, wq.scales, S["w"],
+                                                       wqt.codes, wqt.scales)),
         # dY: ROW16 (dgrad) and COL16 (wgrad) in one pass, one Philox word per element
-        ("quant_dy_row_col_sr", lambda: api.fp4q_quantize(dY, amax["dY"], T, api.ROW16, api.SR, seed, 0,
-                                                          dyq.codes, dyq.scales, S["dy"], dyqt.codes,
-                                                          dyqt.scales)),
+        ("quant_dy_row_col_sr", lambda: api.fp4q_quantize_fmt(dY, amax["dY"], T, api.ROW16, 16, api.UE5M3,
+                                                              pack, api.SR, seed, 0, dyq.codes, dyq.scales,
+                                                              S["dy"], dyqt.codes, dyqt.scales)),
         ("gemm_fwd", lambda: api.fp4q_linear_fwd(xq, wq, Y)),
         ("gemm_dgrad", lambda: api.fp4q_linear_dgrad(dyq, wqt, dX)),
         ("gemm_wgrad", lambda: api.fp4q_linear_wgrad(dyqt, xqt, dW)),
@@ -265,8 +269,8 @@ def main():
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=side):
             for i in range(reps):
-                api.fp4q_quantize_fmt(Xrot[i % nrot], held, T, api.ROW16, block, fmt, api.RNE, 0, 0,
-                                      vc, vs, qS)
+                api.fp4q_quantize_fmt(Xrot[i % nrot], held, T, api.ROW16, block, fmt, api.PACK_ROWS, api.RNE,
+                                      0, 0, vc, vs, qS)
         g.replay()
         torch.cuda.synchronize()
         a.record()
@@ -275,8 +279,8 @@ def main():
         torch.cuda.synchronize()
         v_us = a.elapsed_time(b) / reps * 1e3
         v_bytes = Mq * Kq * (2 + 0.5 + 1 / block)
-        xv, _, _ = api.quantize(X, amax["X"], T, api.ROW16, block=block, scale_fmt=fmt)
-        wv, _, _ = api.quantize(W, amax["W"], T, api.TILE16x16, block=block, scale_fmt=fmt)
+        xv, _, _ = api.quantize(X, amax["X"], T, api.ROW16, block=block, scale_fmt=fmt, pack=pack)
+        wv, _, _ = api.quantize(W, amax["W"], T, api.TILE16x16, block=block, scale_fmt=fmt, pack=pack)
         api.fp4q_linear_fwd(xv, wv, Y)
         a.record()
         for _ in range(3):
@@ -319,15 +323,16 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp16",
         "data": "synthetic",
         "config": {"workload": "ffn_up_step: fwd+dgrad+wgrad refresh step, X 16384x4096 bf16 "
                                "(t3 outlier channels), W 14336x4096 bf16 N(0,0.02) 16x16 blocks, "
                                "dY 16384x14336 bf16 log-uniform with SR",
-                   "M": M, "N": N, "K": K, "target": T, "parallelism": "none (1 GPU)"},
+                   "M": M, "N": N, "K": K, "target": T, "pack": args.pack,
+                   "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "mfma", "kernel": "gemm_kernel (fwd/dgrad/wgrad average)",
-                     "achieved": round(gemm_tflops, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(gemm_tflops / BF16_PEAK_TFLOPS, 4), "traffic": traffic},
+                     "achieved": round(gemm_tflops, 2), "peak": MFMA16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(gemm_tflops / MFMA16_PEAK_TFLOPS, 4), "traffic": traffic},
         "kernels_us": {k: round(v, 2) for k, v in kern.items()},
         "codec_gbs": {k: round(v, 1) for k, v in codec_gbs.items()},
         "quantize_only": {"workload": "8192x4096 bf16 ROW16 RNE, held amax", "us": round(q_us, 2),
@@ -337,7 +342,7 @@ def main():
             "probe_gemm_fwd": {"what": "fwd GEMM with the probe-matched accumulation (64-wide slices, "
                                        "toward-zero slice additions, 1/1024 snap)",
                                "us": round(probe_us, 1), "TFLOP/s": round(probe_tflops, 1),
-                               "frac_bf16_peak": round(probe_tflops / BF16_PEAK_TFLOPS, 4)},
+                               "frac_bf16_peak": round(probe_tflops / MFMA16_PEAK_TFLOPS, 4)},
             "variants": variants,
             "fp4linear_step": {"what": "FP4Linear module fwd+bwd through torch autograd on the same "
                                        "shapes, held-amax steps of a D = 50 schedule (no amax "

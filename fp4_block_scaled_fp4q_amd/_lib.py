@@ -20,6 +20,7 @@ F32, BF16 = 0, 1
 RNE, SR = 0, 1
 ROW16, COL16, TILE16x16 = 0, 1, 2
 UE5M3, E4M3 = 0, 1
+PACK_ROWS, PACK_K64 = 0, 1
 
 # every entry point include/fp4q.h declares
 EXPORTS = ("fp4q_abi_version", "fp4q_status_str", "fp4q_amax", "fp4q_quantize", "fp4q_quantize_fmt",
@@ -32,7 +33,7 @@ class QTensorC(ctypes.Structure):
     _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p),
                 ("enc_scale", ctypes.c_void_p), ("rows", ctypes.c_int64),
                 ("cols", ctypes.c_int64), ("layout", ctypes.c_int32), ("block", ctypes.c_int32),
-                ("scale_fmt", ctypes.c_int32)]
+                ("scale_fmt", ctypes.c_int32), ("pack", ctypes.c_int32)]
 
 
 class Fp4qError(RuntimeError):
@@ -66,7 +67,7 @@ def lib() -> ctypes.CDLL:
                                 u64, u32, p, p, p, p, p, p, p]
     L.fp4q_quantize_fmt.restype = ctypes.c_int
     L.fp4q_quantize_fmt.argtypes = [p, ctypes.c_int, i64, i64, i64, p, f, ctypes.c_int, i32, ctypes.c_int,
-                                    ctypes.c_int, u64, u32, p, p, p, p, p, p, p]
+                                    i32, ctypes.c_int, u64, u32, p, p, p, p, p, p, p]
     L.fp4q_dequant.restype = ctypes.c_int
     L.fp4q_dequant.argtypes = [qp, p, ctypes.c_int, p]
     for name in ("fp4q_linear_fwd", "fp4q_linear_dgrad", "fp4q_linear_wgrad"):

@@ -13,13 +13,13 @@ from dataclasses import dataclass
 import torch
 
 from . import _lib
-from ._lib import (BF16, COL16, E4M3, F32, QTensorC, RNE, ROW16, SR, TILE16x16, UE5M3, check,
-                   lib)
+from ._lib import (BF16, COL16, E4M3, F32, PACK_K64, PACK_ROWS, QTensorC, RNE, ROW16, SR, TILE16x16,
+                   UE5M3, check, lib)
 
 __all__ = ["QTensor", "fp4q_amax", "fp4q_quantize", "fp4q_quantize_fmt", "fp4q_dequant",
            "fp4q_linear_fwd", "fp4q_linear_dgrad", "fp4q_linear_wgrad", "fp4q_linear_probe",
            "quantize", "amax", "dequant", "ROW16", "COL16", "TILE16x16", "RNE", "SR", "F32", "BF16",
-           "UE5M3", "E4M3"]
+           "UE5M3", "E4M3", "PACK_ROWS", "PACK_K64"]
 
 
 def _dtype_code(t: torch.Tensor) -> int:
@@ -56,19 +56,24 @@ def _ptr(t: torch.Tensor | None) -> int | None:
 
 @dataclass
 class QTensor:
-    """A quantized operand on the device (see fp4q_qtensor)."""
-    codes: torch.Tensor      # uint8 [rows, cols/2]
-    scales: torch.Tensor     # uint8 [rows, cols/B] (ROW16) or [rows/B, cols/B] (TILE), B = block
+    """A quantized operand on the device (see fp4q_qtensor).
+
+    Row-major packing: codes uint8 [rows, cols/2], scales [SR, cols/B] with
+    SR = rows (ROW16) or rows/B (TILE), B = block. K64 packing: the same
+    bytes as [cols/64, rows, 32] codes and [cols/64, SR, 64/B] scales."""
+    codes: torch.Tensor
+    scales: torch.Tensor
     enc_scale: torch.Tensor  # float32 [1]: the tensor scale S
     rows: int
     cols: int
     layout: int              # ROW16 or TILE16x16
     block: int = 16          # 16, or 32 for the block-32 variant
     scale_fmt: int = UE5M3   # UE5M3, or E4M3 (NVFP4's scale format)
+    pack: int = PACK_ROWS    # PACK_ROWS or PACK_K64
 
     def c(self) -> QTensorC:
         return QTensorC(self.codes.data_ptr(), self.scales.data_ptr(), self.enc_scale.data_ptr(),
-                        self.rows, self.cols, self.layout, self.block, self.scale_fmt)
+                        self.rows, self.cols, self.layout, self.block, self.scale_fmt, self.pack)
 
 
 # ---------------------------------------------------------------- entry points
@@ -92,14 +97,14 @@ def fp4q_quantize(x: torch.Tensor, amax_held: torch.Tensor, target: float, layou
 
 
 def fp4q_quantize_fmt(x: torch.Tensor, amax_held: torch.Tensor, target: float, layout: int,
-                      block: int, scale_fmt: int, rnd: int, seed: int, subseq: int,
+                      block: int, scale_fmt: int, pack: int, rnd: int, seed: int, subseq: int,
                       codes: torch.Tensor, scales: torch.Tensor,
                       enc_scale_out: torch.Tensor | None = None, codes_t: torch.Tensor | None = None,
                       scales_t: torch.Tensor | None = None, diag: torch.Tensor | None = None) -> None:
     _dev2d(x, "x")
     st = lib().fp4q_quantize_fmt(x.data_ptr(), _dtype_code(x), x.shape[0], x.shape[1], _ld(x),
                                  amax_held.data_ptr(), float(target), int(layout), int(block),
-                                 int(scale_fmt), int(rnd), int(seed) & (2 ** 64 - 1),
+                                 int(scale_fmt), int(pack), int(rnd), int(seed) & (2 ** 64 - 1),
                                  int(subseq) & 0xFFFFFFFF, codes.data_ptr(), scales.data_ptr(),
                                  _ptr(enc_scale_out), _ptr(codes_t), _ptr(scales_t), _ptr(diag),
                                  _stream())
@@ -155,9 +160,22 @@ def amax(x: torch.Tensor) -> torch.Tensor:
     return out
 
 
+def operand_buffers(rows: int, cols: int, tile: bool, block: int = 16, pack: int = PACK_ROWS,
+                    device: torch.device | str = "cuda"):
+    """Allocate (codes, scales) of an operand with `rows` rows contiguous
+    along `cols`, shaped for its packing (see QTensor)."""
+    u8 = dict(dtype=torch.uint8, device=device)
+    SR = rows // block if tile else rows
+    if pack == PACK_K64:
+        return (torch.empty((cols // 64, rows, 32), **u8),
+                torch.empty((cols // 64, SR, 64 // block), **u8))
+    return torch.empty((rows, cols // 2), **u8), torch.empty((SR, cols // block), **u8)
+
+
 def quantize(x: torch.Tensor, amax_held: torch.Tensor, target: float = 448.0, layout: int = ROW16,
              rnd: int = RNE, seed: int = 0, subseq: int = 0, transposed: bool = False,
-             with_diag: bool = False, block: int = 16, scale_fmt: int = UE5M3):
+             with_diag: bool = False, block: int = 16, scale_fmt: int = UE5M3,
+             pack: int = PACK_ROWS):
     """Allocate outputs and run fp4q_quantize_fmt.
 
     Returns (q, qt, diag): q is the operand as the GEMMs read it (for COL16,
@@ -165,32 +183,28 @@ def quantize(x: torch.Tensor, amax_held: torch.Tensor, target: float = 448.0, la
     other orientation (TILE: the transposed tile copy; ROW16: the COL16
     operand [cols, rows] of the same tensor), else None; diag the int32[2]
     repair counts or None. block (16 or 32) and scale_fmt (UE5M3 or E4M3)
-    select the variant.
+    select the variant, pack the memory packing of every output.
     """
     _dev2d(x, "x")
     R, C = x.shape
     B = block
     dev = x.device
-    u8 = dict(dtype=torch.uint8, device=dev)
     S = torch.empty(1, dtype=torch.float32, device=dev)
     if layout == COL16:
-        codes = torch.empty((C, R // 2), **u8)
-        scales = torch.empty((C, R // B), **u8)
+        codes, scales = operand_buffers(C, R, False, B, pack, dev)
     else:
-        codes = torch.empty((R, C // 2), **u8)
-        scales = torch.empty((R, C // B) if layout == ROW16 else (R // B, C // B), **u8)
+        codes, scales = operand_buffers(R, C, layout == TILE16x16, B, pack, dev)
     codes_t = scales_t = None
     if transposed:
-        codes_t = torch.empty((C, R // 2), **u8)
-        scales_t = torch.empty((C // B, R // B) if layout == TILE16x16 else (C, R // B), **u8)
+        codes_t, scales_t = operand_buffers(C, R, layout == TILE16x16, B, pack, dev)
     diag = torch.empty(2, dtype=torch.int32, device=dev) if with_diag else None
-    fp4q_quantize_fmt(x, amax_held, target, layout, block, scale_fmt, rnd, seed, subseq, codes,
+    fp4q_quantize_fmt(x, amax_held, target, layout, block, scale_fmt, pack, rnd, seed, subseq, codes,
                       scales, S, codes_t, scales_t, diag)
     if layout == COL16:
-        q = QTensor(codes, scales, S, C, R, ROW16, B, scale_fmt)
+        q = QTensor(codes, scales, S, C, R, ROW16, B, scale_fmt, pack)
     else:
-        q = QTensor(codes, scales, S, R, C, layout, B, scale_fmt)
-    qt = QTensor(codes_t, scales_t, S, C, R, layout, B, scale_fmt) if transposed else None
+        q = QTensor(codes, scales, S, R, C, layout, B, scale_fmt, pack)
+    qt = QTensor(codes_t, scales_t, S, C, R, layout, B, scale_fmt, pack) if transposed else None
     return q, qt, diag
 
 

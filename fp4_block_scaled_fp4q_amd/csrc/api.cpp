@@ -35,7 +35,9 @@ fp4q_status check_operand(const fp4q_qtensor* q) {
   if (q->layout != FP4Q_ROW16 && q->layout != FP4Q_TILE16x16) return FP4Q_E_ARG;
   if (q->block != 16 && q->block != 32) return FP4Q_E_ARG;
   if (q->scale_fmt != FP4Q_UE5M3 && q->scale_fmt != FP4Q_E4M3) return FP4Q_E_ARG;
+  if (q->pack != FP4Q_PACK_ROWS && q->pack != FP4Q_PACK_K64) return FP4Q_E_ARG;
   if (q->cols % q->block) return FP4Q_E_SHAPE;
+  if (q->pack == FP4Q_PACK_K64 && q->cols % 64) return FP4Q_E_SHAPE;
   if (q->layout == FP4Q_TILE16x16 && q->rows % q->block) return FP4Q_E_SHAPE;
   if (!q->enc_scale) return FP4Q_E_NULL;
   if (q->rows > 0 && q->cols > 0 && (!q->codes || !q->scales)) return FP4Q_E_NULL;
@@ -53,6 +55,7 @@ fp4q::QOperand to_operand(const fp4q_qtensor* q) {
   o.tile = q->layout == FP4Q_TILE16x16 ? 1 : 0;
   o.block = q->block;
   o.scale_fmt = q->scale_fmt;
+  o.pack = q->pack;
   return o;
 }
 
@@ -65,6 +68,7 @@ fp4q_status gemm(const fp4q_qtensor* a, const fp4q_qtensor* b, void* y, fp4q_dty
   const int es = elem_size(yt);
   if (!es) return FP4Q_E_DTYPE;
   if (a->cols != b->cols) return FP4Q_E_SHAPE;
+  if (a->pack != b->pack) return FP4Q_E_ARG;
   if (a->rows > 0 && b->rows > 0 && !y) return FP4Q_E_NULL;
   const int64_t tm = (a->rows + 127) / 128, tn = (b->rows + 127) / 128;
   if (tm > 0 && tn > (0x7FFFFFFF / 512) / tm) return FP4Q_E_SHAPE;
@@ -111,8 +115,9 @@ fp4q_status fp4q_amax(const void* x, fp4q_dtype xt, int64_t rows, int64_t cols, 
 
 fp4q_status fp4q_quantize_fmt(const void* x, fp4q_dtype xt, int64_t rows, int64_t cols,
                               int64_t ld, const float* amax_held, float target, fp4q_layout layout,
-                              int32_t block, fp4q_scale_fmt scale_fmt, fp4q_round rnd,
-                              uint64_t seed, uint32_t subseq, uint8_t* codes, uint8_t* scales,
+                              int32_t block, fp4q_scale_fmt scale_fmt, int32_t pack,
+                              fp4q_round rnd, uint64_t seed, uint32_t subseq, uint8_t* codes,
+                              uint8_t* scales,
                               float* enc_scale_out, uint8_t* codes_t, uint8_t* scales_t,
                               int32_t* diag, void* stream) {
   const int es = elem_size(xt);
@@ -120,6 +125,7 @@ fp4q_status fp4q_quantize_fmt(const void* x, fp4q_dtype xt, int64_t rows, int64_
   if (layout != FP4Q_ROW16 && layout != FP4Q_COL16 && layout != FP4Q_TILE16x16) return FP4Q_E_ARG;
   if (block != 16 && block != 32) return FP4Q_E_ARG;
   if (scale_fmt != FP4Q_UE5M3 && scale_fmt != FP4Q_E4M3) return FP4Q_E_ARG;
+  if (pack != FP4Q_PACK_ROWS && pack != FP4Q_PACK_K64) return FP4Q_E_ARG;
   if (rnd != FP4Q_RNE && rnd != FP4Q_SR) return FP4Q_E_ARG;
   if (!(target > 0.0f) || !std::isfinite(target)) return FP4Q_E_ARG;
   if ((codes_t == nullptr) != (scales_t == nullptr)) return FP4Q_E_ARG;
@@ -131,6 +137,12 @@ fp4q_status fp4q_quantize_fmt(const void* x, fp4q_dtype xt, int64_t rows, int64_
   if (layout != FP4Q_COL16 && cols % block) return FP4Q_E_SHAPE;
   if (layout != FP4Q_ROW16 && rows % block) return FP4Q_E_SHAPE;
   if (layout == FP4Q_COL16 && cols % 8) return FP4Q_E_ALIGN;
+  if (pack == FP4Q_PACK_K64) {
+    // every output's contraction length: cols for ROW16 and TILE, rows for
+    // COL16 and for the second (transposed) outputs
+    if (layout != FP4Q_COL16 && cols % 64) return FP4Q_E_SHAPE;
+    if ((layout == FP4Q_COL16 || codes_t) && rows % 64) return FP4Q_E_SHAPE;
+  }
   const bool nonempty = rows > 0 && cols > 0;
   if (nonempty) {
     if (!x || !codes || !scales) return FP4Q_E_NULL;
@@ -161,6 +173,7 @@ fp4q_status fp4q_quantize_fmt(const void* x, fp4q_dtype xt, int64_t rows, int64_
   a.layout = (int)layout;
   a.block = block;
   a.scale_fmt = (int)scale_fmt;
+  a.pack = pack;
   a.sr = rnd == FP4Q_SR ? 1 : 0;
   a.seed = seed;
   a.subseq = subseq;
@@ -178,9 +191,9 @@ fp4q_status fp4q_quantize(const void* x, fp4q_dtype xt, int64_t rows, int64_t co
                           fp4q_round rnd, uint64_t seed, uint32_t subseq, uint8_t* codes,
                           uint8_t* scales, float* enc_scale_out, uint8_t* codes_t,
                           uint8_t* scales_t, int32_t* diag, void* stream) {
-  return fp4q_quantize_fmt(x, xt, rows, cols, ld, amax_held, target, layout, 16, FP4Q_UE5M3, rnd,
-                           seed, subseq, codes, scales, enc_scale_out, codes_t, scales_t, diag,
-                           stream);
+  return fp4q_quantize_fmt(x, xt, rows, cols, ld, amax_held, target, layout, 16, FP4Q_UE5M3,
+                           FP4Q_PACK_ROWS, rnd, seed, subseq, codes, scales, enc_scale_out, codes_t,
+                           scales_t, diag, stream);
 }
 
 fp4q_status fp4q_dequant(const fp4q_qtensor* q, void* out, fp4q_dtype ot, void* stream) {

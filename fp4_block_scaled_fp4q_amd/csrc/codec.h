@@ -206,6 +206,20 @@ __device__ __forceinline__ U4 sr_words(uint64_t j, uint32_t subseq, uint64_t see
   return philox4x32_10(c, (uint32_t)seed, (uint32_t)(seed >> 32));
 }
 
+// Byte offsets in an operand's packing. Row-major: code byte j of row r at
+// r * C/2 + j, scale j of scale row s at s * nj + j. K64 (the contraction in
+// tiles of 64 elements, each tile holding all rows back to back): code byte
+// j of row r at (j / 32) * (R * 32) + r * 32 + j % 32 for R rows; scale j of
+// scale row s at (j / n) * (SR * n) + s * n + j % n for SR scale rows and
+// n = 64 / block scales per row and tile.
+__device__ __forceinline__ int64_t code_offset(int64_t r, int64_t j, int64_t R, int64_t C, bool k64) {
+  return k64 ? (j >> 5) * (R << 5) + (r << 5) + (j & 31) : r * (C >> 1) + j;
+}
+template <int kN>
+__device__ __forceinline__ int64_t scale_offset(int64_t s, int64_t j, int64_t SR, int64_t nj, bool k64) {
+  return k64 ? (j / kN) * (SR * kN) + s * kN + j % kN : s * nj + j;
+}
+
 // bf16 -> fp32 widening of a packed pair.
 __device__ __forceinline__ float bf16_lo(uint32_t d) { return u2f(d << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t d) { return u2f(d & 0xFFFF0000u); }

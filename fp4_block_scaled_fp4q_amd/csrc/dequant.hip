@@ -26,16 +26,20 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict_
                                                       const uint8_t* __restrict__ scales,
                                                       const float* __restrict__ enc_scale,
                                                       int64_t rows, int64_t cols, int tile,
-                                                      int block, int e4m3, void* __restrict__ out,
-                                                      int out_es) {
+                                                      int block, int e4m3, int k64,
+                                                      void* __restrict__ out, int out_es) {
   const int64_t words_per_row = cols / 8;
   const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (g >= rows * words_per_row) return;
   const int64_t r = g / words_per_row;
   const int64_t w = g - r * words_per_row;
-  const uint32_t d = reinterpret_cast<const uint32_t*>(codes + r * (cols / 2))[w];
+  const uint32_t d = *reinterpret_cast<const uint32_t*>(codes + code_offset(r, 4 * w, rows, cols, k64));
   const int64_t srow = tile ? r / block : r;
-  const float dec = scale_value(scales[srow * (cols / block) + (w * 8) / block], e4m3 != 0);
+  const int64_t nsrow = tile ? rows / block : rows;
+  const int64_t j = (w * 8) / block;
+  const int64_t si = block == 32 ? scale_offset<2>(srow, j, nsrow, cols / block, k64)
+                                 : scale_offset<4>(srow, j, nsrow, cols / block, k64);
+  const float dec = scale_value(scales[si], e4m3 != 0);
   const float S = *enc_scale;
   float v[8];
 #pragma unroll
@@ -58,7 +62,8 @@ hipError_t launch_dequant(const QOperand& q, void* out, int out_es, hipStream_t 
   const int64_t n = q.rows * (q.cols / 8);
   if (n == 0) return hipSuccess;
   hipLaunchKernelGGL(dequant_kernel, dim3((uint32_t)((n + 255) / 256)), dim3(256), 0, s, q.codes,
-                     q.scales, q.enc_scale, q.rows, q.cols, q.tile, q.block, q.scale_fmt, out, out_es);
+                     q.scales, q.enc_scale, q.rows, q.cols, q.tile, q.block, q.scale_fmt, q.pack, out,
+                     out_es);
   return hipGetLastError();
 }
 

@@ -95,24 +95,31 @@ __device__ __forceinline__ uint32_t seg_scale(const RowSeg& g, int j, bool blk32
 // to the last row (their products only reach outputs that are not stored),
 // so the load is branch-free. blk32: blocks of 32 (else 16); the second
 // 16-bit scale load repeats the first for blocks of 32, so it stays inside
-// the row.
-template <bool kFmt>
+// the row. kK64: the K64 packing, where a segment is the row's 32 bytes of
+// k tile k0 / 64 and the workgroup's consecutive rows are adjacent.
+template <bool kFmt, bool kK64>
 __device__ __forceinline__ RowSeg load_seg_full(const uint8_t* __restrict__ codes,
                                                 const uint8_t* __restrict__ scales, int64_t rows,
                                                 int64_t K, int tile_shift, bool blk32, int64_t r,
                                                 int64_t k0) {
   r = r < rows ? r : rows - 1;
-  const uint8_t* cp = codes + r * (K / 2) + k0 / 2;
+  const int64_t kt = k0 / BK;
+  const int64_t srows = rows >> tile_shift;
+  const uint8_t* cp = kK64 ? codes + kt * (rows * 32) + r * 32 : codes + r * (K / 2) + k0 / 2;
   RowSeg g;
   g.c0 = *reinterpret_cast<const uint4*>(cp);
   g.c1 = *reinterpret_cast<const uint4*>(cp + 16);
   if (!kFmt) {
-    g.s0 = *reinterpret_cast<const uint32_t*>(scales + (r >> tile_shift) * (K / 16) + k0 / 16);
+    g.s0 = *reinterpret_cast<const uint32_t*>(
+        kK64 ? scales + kt * (srows * 4) + (r >> tile_shift) * 4
+             : scales + (r >> tile_shift) * (K / 16) + k0 / 16);
     g.s1 = 0u;
     return g;
   }
   const int sh = blk32 ? 5 : 4;
-  const uint8_t* sp = scales + (r >> tile_shift) * (K >> sh) + (k0 >> sh);
+  const int n = blk32 ? 2 : 4;  // scale bytes per row and k tile
+  const uint8_t* sp = kK64 ? scales + kt * (srows * n) + (r >> tile_shift) * n
+                           : scales + (r >> tile_shift) * (K >> sh) + (k0 >> sh);
   g.s0 = *reinterpret_cast<const uint16_t*>(sp);
   g.s1 = *reinterpret_cast<const uint16_t*>(blk32 ? sp : sp + 2);
   return g;
@@ -157,12 +164,13 @@ __device__ __forceinline__ RowSeg load_seg_tail(const uint8_t* __restrict__ code
   return g;
 }
 
-template <bool kFullK, bool kFmt>
+template <bool kFullK, bool kFmt, bool kK64>
 __device__ __forceinline__ RowSeg load_seg(const uint8_t* __restrict__ codes,
                                            const uint8_t* __restrict__ scales, int64_t rows,
                                            int64_t K, int tile_shift, bool blk32, int64_t r,
                                            int64_t k0) {
-  return kFullK ? load_seg_full<kFmt>(codes, scales, rows, K, tile_shift, blk32, r, k0)
+  static_assert(kFullK || !kK64, "the K64 packing needs K % 64 == 0");
+  return kFullK ? load_seg_full<kFmt, kK64>(codes, scales, rows, K, tile_shift, blk32, r, k0)
                 : load_seg_tail<kFmt>(codes, scales, rows, K, tile_shift, blk32, r, k0);
 }
 
@@ -242,7 +250,7 @@ constexpr int row_pitch() { return kSwz == 2 ? kChunks + 1 : kChunks; }
 // optionally snaps the sum to multiples of 2^-snap_log2 (ties to even)
 // before applying alpha.
 template <int kBM, int kBN, bool kFullK, bool kF32Out, int kWavesM, int kWavesN, int kSwz, bool kProbe,
-          bool kFmt>
+          bool kFmt, bool kK64>
 __global__ __launch_bounds__(64 * kWavesM * kWavesN) void gemm_kernel(
     const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales, int a_shift,
     const float* __restrict__ a_S, const uint8_t* __restrict__ b_codes,
@@ -306,8 +314,10 @@ __global__ __launch_bounds__(64 * kWavesM * kWavesN) void gemm_kernel(
 #pragma unroll
     for (int i = 0; i < kRows; ++i) {
       const int q = tid + i * kT;
-      g[i] = q < kBM ? load_seg<kFullK, kFmt>(a_codes, a_scales, M, K, a_shift, a_blk32, m0 + q, k0)
-                    : load_seg<kFullK, kFmt>(b_codes, b_scales, N, K, b_shift, b_blk32, n0 + (q - kBM), k0);
+      g[i] = q < kBM
+                 ? load_seg<kFullK, kFmt, kK64>(a_codes, a_scales, M, K, a_shift, a_blk32, m0 + q, k0)
+                 : load_seg<kFullK, kFmt, kK64>(b_codes, b_scales, N, K, b_shift, b_blk32, n0 + (q - kBM),
+                                                k0);
     }
   };
   // one decode8 piece p (0 .. kPieces-1) of block s into buffer `buf`
@@ -553,18 +563,23 @@ int concurrent_workgroups() {
 template <int kBM, int kBN, int kWM, int kWN, int kSW, bool kProbe, bool kFmt>
 hipError_t launch_kernel(const QOperand& a, const QOperand& b, void* y, int y_es, int snap_log2,
                          int fmt, hipStream_t s) {
+  // operands share the packing (checked by the caller); K64 implies K % 64 == 0
+  const bool k64 = a.pack != 0;
   const int64_t M = a.rows, N = b.rows, K = a.cols;
   const int tiles_m = (int)((M + kBM - 1) / kBM);
   const int tiles_n = (int)((N + kBN - 1) / kBN);
   const bool full_k = K % BK == 0;
   const size_t lds_bytes = 2 * (kBM + kBN) * (kSW == 2 ? kChunks + 1 : kChunks) * sizeof(uint4);
   const void* fn;
-  if (full_k)
-    fn = y_es == 4 ? (const void*)gemm_kernel<kBM, kBN, true, true, kWM, kWN, kSW, kProbe, kFmt>
-                   : (const void*)gemm_kernel<kBM, kBN, true, false, kWM, kWN, kSW, kProbe, kFmt>;
+  if (k64)
+    fn = y_es == 4 ? (const void*)gemm_kernel<kBM, kBN, true, true, kWM, kWN, kSW, kProbe, kFmt, true>
+                   : (const void*)gemm_kernel<kBM, kBN, true, false, kWM, kWN, kSW, kProbe, kFmt, true>;
+  else if (full_k)
+    fn = y_es == 4 ? (const void*)gemm_kernel<kBM, kBN, true, true, kWM, kWN, kSW, kProbe, kFmt, false>
+                   : (const void*)gemm_kernel<kBM, kBN, true, false, kWM, kWN, kSW, kProbe, kFmt, false>;
   else
-    fn = y_es == 4 ? (const void*)gemm_kernel<kBM, kBN, false, true, kWM, kWN, kSW, kProbe, kFmt>
-                   : (const void*)gemm_kernel<kBM, kBN, false, false, kWM, kWN, kSW, kProbe, kFmt>;
+    fn = y_es == 4 ? (const void*)gemm_kernel<kBM, kBN, false, true, kWM, kWN, kSW, kProbe, kFmt, false>
+                   : (const void*)gemm_kernel<kBM, kBN, false, false, kWM, kWN, kSW, kProbe, kFmt, false>;
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);
   if (e != hipSuccess) return e;
   // split tail: when the tiles fill the last round of workgroups at most
@@ -590,16 +605,19 @@ hipError_t launch_kernel(const QOperand& a, const QOperand& b, void* y, int y_es
   const dim3 grid((uint32_t)nwg), block(64 * kWM * kWN);
   const int a_shift = a.tile ? (a.block == 32 ? 5 : 4) : 0;
   const int b_shift = b.tile ? (b.block == 32 ? 5 : 4) : 0;
-#define FP4Q_GEMM(FK, F32)                                                                     \
-  hipLaunchKernelGGL((gemm_kernel<kBM, kBN, FK, F32, kWM, kWN, kSW, kProbe, kFmt>), grid, block, \
-                     lds_bytes, s, a.codes, a.scales, a_shift, a.enc_scale, b.codes, b.scales,    \
+#define FP4Q_GEMM(FK, F32, K64)                                                                     \
+  hipLaunchKernelGGL((gemm_kernel<kBM, kBN, FK, F32, kWM, kWN, kSW, kProbe, kFmt, K64>), grid, block, \
+                     lds_bytes, s, a.codes, a.scales, a_shift, a.enc_scale, b.codes, b.scales,         \
                      b_shift, b.enc_scale, M, N, K, tiles_m, tiles_n, snap_log2, fmt, split_local, y)
-  if (full_k) {
-    if (y_es == 4) FP4Q_GEMM(true, true);
-    else FP4Q_GEMM(true, false);
+  if (k64) {
+    if (y_es == 4) FP4Q_GEMM(true, true, true);
+    else FP4Q_GEMM(true, false, true);
+  } else if (full_k) {
+    if (y_es == 4) FP4Q_GEMM(true, true, false);
+    else FP4Q_GEMM(true, false, false);
   } else {
-    if (y_es == 4) FP4Q_GEMM(false, true);
-    else FP4Q_GEMM(false, false);
+    if (y_es == 4) FP4Q_GEMM(false, true, false);
+    else FP4Q_GEMM(false, false, false);
   }
 #undef FP4Q_GEMM
   return hipGetLastError();

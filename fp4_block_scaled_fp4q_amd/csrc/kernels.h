@@ -21,6 +21,7 @@ struct QuantArgs {
   int layout;  // 0 ROW16, 1 COL16, 2 TILE16x16 (blocks along a row, down a column, square)
   int block;   // 16 or 32
   int scale_fmt;  // 0 UE5M3, 1 E4M3
+  int pack;       // 0 row-major, 1 K64 (tiles of 64 along the contraction)
   int sr;      // 0 RNE, 1 SR
   uint64_t seed;
   uint32_t subseq;
@@ -41,6 +42,7 @@ struct QOperand {
   int tile;  // 0: ROW16 scales [rows][cols/block]; 1: TILE16x16 scales [rows/block][cols/block]
   int block;      // 16 or 32
   int scale_fmt;  // 0 UE5M3, 1 E4M3 (value = UE5M3 value * 256)
+  int pack;       // 0 row-major, 1 K64 (tiles of 64 along the contraction)
 };
 
 hipError_t launch_dequant(const QOperand& q, void* out, int out_es, hipStream_t s);

@@ -160,10 +160,10 @@ __device__ __forceinline__ void store_block_codes(uint8_t* dst, const uint32_t (
 
 template <bool kBF16, bool kSR, int kBlk>
 __global__ __launch_bounds__(kRowThreads) void quant_row_kernel(
-    const uint8_t* __restrict__ x, int64_t cols, int64_t ld_bytes, int segs_per_row,
-    const float* __restrict__ amax_held, float target, int e4m3, uint64_t seed, uint32_t subseq,
-    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, float* __restrict__ enc_out,
-    int32_t* __restrict__ diag) {
+    const uint8_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld_bytes, int segs_per_row,
+    const float* __restrict__ amax_held, float target, int e4m3, int k64, uint64_t seed,
+    uint32_t subseq, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
+    float* __restrict__ enc_out, int32_t* __restrict__ diag) {
   constexpr int es = kBF16 ? 2 : 4;
   constexpr int kOcts = kBlk / 8;
   const int64_t row = blockIdx.x / segs_per_row;
@@ -194,8 +194,8 @@ __global__ __launch_bounds__(kRowThreads) void quant_row_kernel(
     uint32_t cw[kOcts];
 #pragma clang loop unroll(full)
     for (int j = 0; j < kOcts; ++j) cw[j] = encode_oct<kBF16, kSR>(o[j], s.mul, mi, w + 8 * j);
-    store_block_codes<kBlk>(codes + row * (cols / 2) + blk * (kBlk / 2), cw);
-    scales[row * nblk + blk] = (uint8_t)s.code;
+    store_block_codes<kBlk>(codes + code_offset(row, blk * (kBlk / 2), rows, cols, k64), cw);
+    scales[scale_offset<64 / kBlk>(row, blk, rows, nblk, k64)] = (uint8_t)s.code;
     nzero = s.flags & 1u;
     nsat = s.flags >> 1;
   }
@@ -234,8 +234,8 @@ __device__ __forceinline__ uint32_t rne8(const float* v, float mu) {
 template <bool kBF16, bool kSR, bool kRow, int kBlk>
 __global__ __launch_bounds__(kDualThreads<kBlk>()) void quant_dual_kernel(
     const uint8_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld_bytes, int col_tiles,
-    int row_tiles, const float* __restrict__ amax_held, float target, int e4m3, uint64_t seed,
-    uint32_t subseq, uint8_t* __restrict__ codes_r, uint8_t* __restrict__ scales_r,
+    int row_tiles, const float* __restrict__ amax_held, float target, int e4m3, int k64,
+    uint64_t seed, uint32_t subseq, uint8_t* __restrict__ codes_r, uint8_t* __restrict__ scales_r,
     uint8_t* __restrict__ codes_c, uint8_t* __restrict__ scales_c, float* __restrict__ enc_out,
     int32_t* __restrict__ diag) {
   constexpr int es = kBF16 ? 2 : 4;
@@ -287,8 +287,8 @@ __global__ __launch_bounds__(kDualThreads<kBlk>()) void quant_dual_kernel(
       uint32_t cw[kOcts];
 #pragma clang loop unroll(full)
       for (int j = 0; j < kOcts; ++j) cw[j] = encode_oct<kBF16, kSR>(o[j], s.mul, mi, w + 8 * j);
-      store_block_codes<kBlk>(codes_r + gr * (cols / 2) + gc / 2, cw);
-      scales_r[gr * (cols / kBlk) + gc / kBlk] = (uint8_t)s.code;
+      store_block_codes<kBlk>(codes_r + code_offset(gr, gc / 2, rows, cols, k64), cw);
+      scales_r[scale_offset<64 / kBlk>(gr, gc / kBlk, rows, cols / kBlk, k64)] = (uint8_t)s.code;
       nzero += s.flags & 1u;
       nsat += s.flags >> 1;
     }
@@ -344,8 +344,8 @@ __global__ __launch_bounds__(kDualThreads<kBlk>()) void quant_dual_kernel(
 #pragma clang loop unroll(full)
         for (int j = 0; j < kOcts; ++j) cw[j] = rne8(v + 8 * j, s.mul);
       }
-      store_block_codes<kBlk>(codes_c + gc * (rows / 2) + gr0 / 2, cw);
-      scales_c[gc * (rows / kBlk) + gr0 / kBlk] = (uint8_t)s.code;
+      store_block_codes<kBlk>(codes_c + code_offset(gc, gr0 / 2, cols, rows, k64), cw);
+      scales_c[scale_offset<64 / kBlk>(gc, gr0 / kBlk, cols, rows / kBlk, k64)] = (uint8_t)s.code;
       nzero += s.flags & 1u;
       nsat += s.flags >> 1;
     }
@@ -378,8 +378,8 @@ __device__ __forceinline__ void store_col_codes(uint8_t* dst, const uint32_t (&c
 template <bool kBF16, bool kSR, bool kT>
 __global__ __launch_bounds__(kThreads) void quant_tile_kernel(
     const uint8_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld_bytes, int col_groups,
-    int row_groups, const float* __restrict__ amax_held, float target, int e4m3, uint64_t seed,
-    uint32_t subseq, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
+    int row_groups, const float* __restrict__ amax_held, float target, int e4m3, int k64,
+    uint64_t seed, uint32_t subseq, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
     uint8_t* __restrict__ codes_t, uint8_t* __restrict__ scales_t, float* __restrict__ enc_out,
     int32_t* __restrict__ diag) {
   constexpr int es = kBF16 ? 2 : 4;
@@ -424,7 +424,7 @@ __global__ __launch_bounds__(kThreads) void quant_tile_kernel(
       uint32_t w[8];
       if (kSR) words8((uint64_t)(r0 + r) * (uint64_t)cols + (uint64_t)c0, seed, subseq, w);
       const uint32_t word = encode_oct<kBF16, kSR>(v[r], b.mul, mi, w);
-      if (valid) reinterpret_cast<uint32_t*>(codes + (r0 + r) * (cols / 2))[oct] = word;
+      if (valid) *reinterpret_cast<uint32_t*>(codes + code_offset(r0 + r, 4 * oct, rows, cols, k64)) = word;
       if (kT) {
 #pragma clang loop unroll(full)
         for (int j = 0; j < 8; ++j)
@@ -432,18 +432,21 @@ __global__ __launch_bounds__(kThreads) void quant_tile_kernel(
       }
     }
     if (valid && (threadIdx.x & 1) == 0) {
-      scales[(r0 / 16) * (cols / 16) + (oct >> 1)] = (uint8_t)b.code;
-      if (kT) scales_t[(oct >> 1) * (rows / 16) + r0 / 16] = (uint8_t)b.code;
+      scales[scale_offset<4>(r0 / 16, oct >> 1, rows / 16, cols / 16, k64)] = (uint8_t)b.code;
+      if (kT) scales_t[scale_offset<4>(oct >> 1, r0 / 16, cols / 16, rows / 16, k64)] = (uint8_t)b.code;
       nzero += b.flags & 1u;
       nsat += b.flags >> 1;
     }
     }  // st < nsub
   }
   if (kT && valid && nsub > 0) {
-    const bool wide = (rows / 2) % 16 == 0;
+    // K64 runs are 16-byte aligned (each column's 8 * kSub bytes sit inside
+    // one 32-byte tile row)
+    const bool wide = k64 || (rows / 2) % 16 == 0;
 #pragma clang loop unroll(full)
     for (int j = 0; j < 8; ++j)
-      store_col_codes<kSub>(codes_t + (c0 + j) * (rows / 2) + r_begin / 2, tcodes[j], nsub, wide);
+      store_col_codes<kSub>(codes_t + code_offset(c0 + j, r_begin / 2, cols, rows, k64), tcodes[j], nsub,
+                            wide);
   }
   if (diag) add_diag(diag, nzero, nsat);
 }
@@ -458,8 +461,8 @@ __global__ __launch_bounds__(kThreads) void quant_tile_kernel(
 template <bool kBF16, bool kSR, bool kT>
 __global__ __launch_bounds__(kThreads) void quant_tile32_kernel(
     const uint8_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld_bytes, int col_groups,
-    int row_groups, const float* __restrict__ amax_held, float target, int e4m3, uint64_t seed,
-    uint32_t subseq, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
+    int row_groups, const float* __restrict__ amax_held, float target, int e4m3, int k64,
+    uint64_t seed, uint32_t subseq, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
     uint8_t* __restrict__ codes_t, uint8_t* __restrict__ scales_t, float* __restrict__ enc_out,
     int32_t* __restrict__ diag) {
   constexpr int es = kBF16 ? 2 : 4;
@@ -498,7 +501,7 @@ __global__ __launch_bounds__(kThreads) void quant_tile32_kernel(
     uint32_t w[8];
     if (kSR) words8((uint64_t)(r0 + r) * (uint64_t)cols + (uint64_t)c0, seed, subseq, w);
     const uint32_t word = encode_oct<kBF16, kSR>(v, b.mul, mi, w);
-    if (valid) reinterpret_cast<uint32_t*>(codes + (r0 + r) * (cols / 2))[oct] = word;
+    if (valid) *reinterpret_cast<uint32_t*>(codes + code_offset(r0 + r, 4 * oct, rows, cols, k64)) = word;
     if (kT) {
 #pragma clang loop unroll(full)
       for (int j = 0; j < 8; ++j) tcodes[j][r >> 3] |= ((word >> (4 * j)) & 0xFu) << (4 * (r & 7));
@@ -506,14 +509,15 @@ __global__ __launch_bounds__(kThreads) void quant_tile32_kernel(
   }
   uint32_t nzero = 0u, nsat = 0u;
   if (valid && (threadIdx.x & 3) == 0) {
-    scales[(r0 / 32) * (cols / 32) + (oct >> 2)] = (uint8_t)b.code;
-    if (kT) scales_t[(oct >> 2) * (rows / 32) + r0 / 32] = (uint8_t)b.code;
+    scales[scale_offset<2>(r0 / 32, oct >> 2, rows / 32, cols / 32, k64)] = (uint8_t)b.code;
+    if (kT) scales_t[scale_offset<2>(oct >> 2, r0 / 32, cols / 32, rows / 32, k64)] = (uint8_t)b.code;
     nzero = b.flags & 1u;
     nsat = b.flags >> 1;
   }
   if (kT && valid) {
 #pragma clang loop unroll(full)
-    for (int j = 0; j < 8; ++j) store_block_codes<32>(codes_t + (c0 + j) * (rows / 2) + r0 / 2, tcodes[j]);
+    for (int j = 0; j < 8; ++j)
+      store_block_codes<32>(codes_t + code_offset(c0 + j, r0 / 2, cols, rows, k64), tcodes[j]);
   }
   if (diag) add_diag(diag, nzero, nsat);
 }
@@ -523,13 +527,14 @@ hipError_t launch_typed(const QuantArgs& a, hipStream_t s) {
   const uint8_t* x = static_cast<const uint8_t*>(a.x);
   const int64_t ldb = a.ld * a.es;
   const int e4m3 = a.scale_fmt;
+  const int k64 = a.pack;
   const bool both = a.layout == 0 && a.codes_t != nullptr;
   if (a.layout == 0 && !both) {
     const int64_t nblk = a.cols / kBlk;
     const int segs = (int)((nblk + kRowThreads - 1) / kRowThreads);
     hipLaunchKernelGGL((quant_row_kernel<kBF16, kSR, kBlk>), dim3((uint32_t)(a.rows * segs)),
-                       dim3(kRowThreads), 0, s, x, a.cols, ldb, segs, a.amax_held, a.target, e4m3,
-                       a.seed, a.subseq, a.codes, a.scales, a.enc_scale_out, a.diag);
+                       dim3(kRowThreads), 0, s, x, a.rows, a.cols, ldb, segs, a.amax_held, a.target,
+                       e4m3, k64, a.seed, a.subseq, a.codes, a.scales, a.enc_scale_out, a.diag);
     return hipGetLastError();
   }
   if (a.layout == 2) {
@@ -539,12 +544,12 @@ hipError_t launch_typed(const QuantArgs& a, hipStream_t s) {
       if (a.codes_t)
         hipLaunchKernelGGL((quant_tile32_kernel<kBF16, kSR, true>), grid, dim3(kThreads), 0, s, x,
                            a.rows, a.cols, ldb, col_groups, (int)(a.rows / 32), a.amax_held, a.target,
-                           e4m3, a.seed, a.subseq, a.codes, a.scales, a.codes_t, a.scales_t,
+                           e4m3, k64, a.seed, a.subseq, a.codes, a.scales, a.codes_t, a.scales_t,
                            a.enc_scale_out, a.diag);
       else
         hipLaunchKernelGGL((quant_tile32_kernel<kBF16, kSR, false>), grid, dim3(kThreads), 0, s, x,
                            a.rows, a.cols, ldb, col_groups, (int)(a.rows / 32), a.amax_held, a.target,
-                           e4m3, a.seed, a.subseq, a.codes, a.scales, nullptr, nullptr,
+                           e4m3, k64, a.seed, a.subseq, a.codes, a.scales, nullptr, nullptr,
                            a.enc_scale_out, a.diag);
       return hipGetLastError();
     }
@@ -553,11 +558,11 @@ hipError_t launch_typed(const QuantArgs& a, hipStream_t s) {
     const dim3 grid((uint32_t)(col_groups * row_groups));
     if (a.codes_t)
       hipLaunchKernelGGL((quant_tile_kernel<kBF16, kSR, true>), grid, dim3(kThreads), 0, s, x, a.rows,
-                         a.cols, ldb, col_groups, row_groups, a.amax_held, a.target, e4m3, a.seed,
+                         a.cols, ldb, col_groups, row_groups, a.amax_held, a.target, e4m3, k64, a.seed,
                          a.subseq, a.codes, a.scales, a.codes_t, a.scales_t, a.enc_scale_out, a.diag);
     else
       hipLaunchKernelGGL((quant_tile_kernel<kBF16, kSR, false>), grid, dim3(kThreads), 0, s, x, a.rows,
-                         a.cols, ldb, col_groups, row_groups, a.amax_held, a.target, e4m3, a.seed,
+                         a.cols, ldb, col_groups, row_groups, a.amax_held, a.target, e4m3, k64, a.seed,
                          a.subseq, a.codes, a.scales, nullptr, nullptr, a.enc_scale_out, a.diag);
     return hipGetLastError();
   }
@@ -568,11 +573,11 @@ hipError_t launch_typed(const QuantArgs& a, hipStream_t s) {
   if (both) {
     // ROW outputs in codes/scales, COL outputs in codes_t/scales_t
     hipLaunchKernelGGL((quant_dual_kernel<kBF16, kSR, true, kBlk>), grid, block, 0, s, x, a.rows,
-                       a.cols, ldb, col_tiles, row_tiles, a.amax_held, a.target, e4m3, a.seed,
+                       a.cols, ldb, col_tiles, row_tiles, a.amax_held, a.target, e4m3, k64, a.seed,
                        a.subseq, a.codes, a.scales, a.codes_t, a.scales_t, a.enc_scale_out, a.diag);
   } else {
     hipLaunchKernelGGL((quant_dual_kernel<kBF16, kSR, false, kBlk>), grid, block, 0, s, x, a.rows,
-                       a.cols, ldb, col_tiles, row_tiles, a.amax_held, a.target, e4m3, a.seed,
+                       a.cols, ldb, col_tiles, row_tiles, a.amax_held, a.target, e4m3, k64, a.seed,
                        a.subseq, nullptr, nullptr, a.codes, a.scales, a.enc_scale_out, a.diag);
   }
   return hipGetLastError();

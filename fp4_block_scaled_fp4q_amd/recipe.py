@@ -14,6 +14,10 @@ Pretraining", §5.1-§5.2 and the quantized-inference appendix).
 * Inference: a weight's amax is measured once and then held; activations
   use a delayed cache started from the first batch (refreshed on the same
   period, counted over inference calls).
+* Operands are stored in the K64 packing (contiguous 64-element k tiles,
+  which the GEMM reads in one run per tile) whenever every contraction
+  length involved is a multiple of 64, else row-major; the packing changes
+  no value.
 
 Everything on the data path runs in libfp4q.so (fp4q_amax, fp4q_quantize*,
 fp4q_linear_*); this module only keeps state and calls it. Nothing here
@@ -37,6 +41,7 @@ class Fp4Recipe:
     block: int = 16                   # 16, or 32 (the block-32 variant)
     scale_fmt: int = api.UE5M3        # UE5M3, or E4M3 (NVFP4's scale format)
     seed: int = 0                     # Philox key of this module's dY stochastic rounding
+    pack: int = api.PACK_K64          # memory packing (row-major where a length is not % 64)
 
     def t_dy_wgrad(self) -> float:
         return self.target if self.target_dy_wgrad is None else float(self.target_dy_wgrad)
@@ -95,7 +100,12 @@ class _Fp4LinearFn(torch.autograd.Function):
             st.weight_measured = True
         else:
             aw = st.amax_w.value  # inference: the weight's amax is measured once
-        kw = dict(block=r.block, scale_fmt=r.scale_fmt)
+        M, K, N = x2.shape[0], x2.shape[1], weight.shape[0]
+        # every contraction the packing must serve: K (fwd), and with a
+        # backward N (dgrad) and M (wgrad)
+        lengths = (K, N, M) if need_grad else (K,)
+        pack = api.PACK_K64 if r.pack == api.PACK_K64 and all(n % 64 == 0 for n in lengths) else api.PACK_ROWS
+        kw = dict(block=r.block, scale_fmt=r.scale_fmt, pack=pack)
         # X: ROW (fwd) and, when a backward follows, COL (wgrad) in one pass
         xq, xqt, _ = api.quantize(x2, ax, r.target, api.ROW16, api.RNE, transposed=need_grad, **kw)
         wq, wqt, _ = api.quantize(weight, aw, r.target, api.TILE16x16, api.RNE, transposed=need_grad,
@@ -110,6 +120,7 @@ class _Fp4LinearFn(torch.autograd.Function):
             ctx.x_dtype = x.dtype
             ctx.w_dtype = weight.dtype
             ctx.xqt, ctx.wqt = xqt, wqt
+            ctx.pack = pack
         if training:
             st.step += 1
         else:
@@ -127,7 +138,7 @@ class _Fp4LinearFn(torch.autograd.Function):
         if not dy2.is_contiguous():
             dy2 = dy2.contiguous()
         ady = st.amax_dy.update(dy2, ctx.refresh)
-        kw = dict(block=r.block, scale_fmt=r.scale_fmt)
+        kw = dict(block=r.block, scale_fmt=r.scale_fmt, pack=ctx.pack)
         seed, subseq = r.seed, ctx.step & 0xFFFFFFFF
         t_wg = r.t_dy_wgrad()
         if t_wg == r.target:
@@ -190,4 +201,5 @@ class FP4Linear(torch.nn.Module):
     def extra_repr(self) -> str:
         r = self.recipe
         return (f"in_features={self.in_features}, out_features={self.out_features}, D={r.refresh_period}, "
-                f"T={r.target}, T_dy_wgrad={r.t_dy_wgrad()}, block={r.block}, scale_fmt={r.scale_fmt}")
+                f"T={r.target}, T_dy_wgrad={r.t_dy_wgrad()}, block={r.block}, scale_fmt={r.scale_fmt}, "
+                f"pack={r.pack}")

@@ -32,7 +32,7 @@
 extern "C" {
 #endif
 
-#define FP4Q_ABI_VERSION 2
+#define FP4Q_ABI_VERSION 3
 
 typedef enum {
     FP4Q_OK = 0,
@@ -67,13 +67,30 @@ typedef enum {
  * 0x00..0x7E: 2^-9 .. 448, the same code's UE5M3 value times 256). */
 typedef enum { FP4Q_UE5M3 = 0, FP4Q_E4M3 = 1 } fp4q_scale_fmt;
 
+/* Memory packing of an operand's codes and scales. The pages fix what is
+ * stored (E2M1 codes two per byte, element 2j in bits 3:0 and 2j+1 in bits
+ * 7:4 of byte j of a row; one scale byte per block), not where it lives.
+ *  FP4Q_PACK_ROWS: row-major, as the shapes in fp4q_layout give them.
+ *  FP4Q_PACK_K64: the contraction axis cut into tiles of 64 elements; tile t
+ *    holds every row's 32 code bytes back to back, then the next tile:
+ *    byte j of row r at (j / 32) * (R * 32) + r * 32 + j % 32 for an operand
+ *    of R rows. Scales likewise with 64 / B bytes per row and tile: scale j
+ *    of scale row s at (j / n) * (SR * n) + s * n + j % n, n = 64 / B, SR the
+ *    number of scale rows. The buffer sizes equal the row-major ones. A
+ *    GEMM workgroup then reads its rows' slice of one k tile as one
+ *    contiguous run, and the COL16 output of a quantize is written in
+ *    contiguous runs too. Needs the contraction length (cols of the
+ *    operand) to be a multiple of 64. */
+typedef enum { FP4Q_PACK_ROWS = 0, FP4Q_PACK_K64 = 1 } fp4q_pack;
+
 /* One quantized operand as the GEMMs read it: `rows` x `cols` logical
  * elements, contiguous along `cols` (the contraction). layout is FP4Q_ROW16
  * (scales [rows][cols/B]; also what FP4Q_COL16 produces for the transpose)
  * or FP4Q_TILE16x16 (scales [rows/B][cols/B]), B = block (16 or 32);
  * scale_fmt an fp4q_scale_fmt. enc_scale points to the device fp32 tensor
  * scale S written by fp4q_quantize. codes must be 8-byte aligned and scales
- * 4-byte aligned. */
+ * 4-byte aligned. pack is an fp4q_pack; the two operands of a GEMM must share
+ * it, and FP4Q_PACK_K64 needs cols % 64 == 0. */
 typedef struct {
     const uint8_t *codes;
     const uint8_t *scales;
@@ -83,6 +100,7 @@ typedef struct {
     int32_t layout;
     int32_t block;
     int32_t scale_fmt;
+    int32_t pack;
 } fp4q_qtensor;
 
 int fp4q_abi_version(void);
@@ -145,26 +163,32 @@ fp4q_status fp4q_quantize(const void *x, fp4q_dtype xt, int64_t rows, int64_t co
  * (shapes, divisibility, the TILE transposed copy with B x B tiles, the ROW
  * plus COL single pass); for E4M3 the nearest-code encode saturates once raw
  * exceeds 464 (to 0x7E = 448) and a zero-rounded scale repairs to 0x01
- * (2^-9). fp4q_quantize is this call with block 16 and FP4Q_UE5M3.
+ * (2^-9). pack (an fp4q_pack) applies to every output (codes, scales and
+ * the codes_t / scales_t pair); FP4Q_PACK_K64 needs the contraction length
+ * of each output to be a multiple of 64: cols for FP4Q_ROW16 and
+ * FP4Q_TILE16x16, rows for FP4Q_COL16 and for the codes_t outputs.
+ * fp4q_quantize is this call with block 16, FP4Q_UE5M3 and FP4Q_PACK_ROWS.
  */
 fp4q_status fp4q_quantize_fmt(const void *x, fp4q_dtype xt, int64_t rows, int64_t cols,
                               int64_t ld, const float *amax_held, float target,
                               fp4q_layout layout, int32_t block, fp4q_scale_fmt scale_fmt,
-                              fp4q_round rnd, uint64_t seed, uint32_t subseq, uint8_t *codes,
-                              uint8_t *scales, float *enc_scale_out, uint8_t *codes_t,
-                              uint8_t *scales_t, int32_t *diag, void *stream);
+                              int32_t pack, fp4q_round rnd, uint64_t seed, uint32_t subseq,
+                              uint8_t *codes, uint8_t *scales, float *enc_scale_out,
+                              uint8_t *codes_t, uint8_t *scales_t, int32_t *diag,
+                              void *stream);
 
 /*
  * Dequantize q into out ([q->rows, q->cols], row-major, dtype ot):
  * x_hat = RN_fp32((e2m1 * dec) / S), then RNE to bf16 for FP4Q_BF16 (§6 of
  * the page: the emulation decodes operands exactly; S is removed after).
- * q->cols % q->block == 0; out 16-byte aligned.
+ * q->cols % q->block == 0 (% 64 for FP4Q_PACK_K64); out 16-byte aligned.
  */
 fp4q_status fp4q_dequant(const fp4q_qtensor *q, void *out, fp4q_dtype ot, void *stream);
 
 /*
  * The emulated FP4 linear layer (§6 of the page): the contraction of the
- * decoded operands in bf16 MFMA with fp32 accumulation, times
+ * decoded operands (exact in binary16 after a power-of-two scaling, which
+ * alpha undoes) in f16 MFMA with fp32 accumulation, times
  * alpha = 1 / (Sa Sb) (computed in double), rounded once to fp32 and then,
  * for a bf16 output, once more (RNE). Outputs are row-major and contiguous.
  *  fwd:   y[M, N]  = Xq[M, K] . Wq[N, K]^T      xq: X ROW16; wq: W TILE16x16
@@ -175,7 +199,8 @@ fp4q_status fp4q_dequant(const fp4q_qtensor *q, void *out, fp4q_dtype ot, void *
  * In each, both operands must have equal `cols` (the contraction length,
  * a multiple of 16 and of each operand's block size) and `rows` a multiple of
  * the block size when their layout is TILE. The two operands may use
- * different block sizes and scale formats.
+ * different block sizes and scale formats; they must share the packing
+ * (FP4Q_E_ARG otherwise).
  */
 fp4q_status fp4q_linear_fwd(const fp4q_qtensor *xq, const fp4q_qtensor *wq, void *y,
                             fp4q_dtype yt, void *stream);

@@ -24,13 +24,28 @@ def dev_scalar(v: float) -> torch.Tensor:
     return torch.tensor([v], dtype=torch.float32, device=DEV)
 
 
+def unpack_k64(a: np.ndarray) -> np.ndarray:
+    """Row-major view of a K64-packed code or scale array: [tiles, rows, n]
+    (n bytes of each row per 64-element tile) -> [rows, tiles * n]."""
+    t, r, n = a.shape
+    return np.ascontiguousarray(a.transpose(1, 0, 2)).reshape(r, t * n)
+
+
+def host_rows(t: torch.Tensor, pack: int) -> np.ndarray:
+    """A device code or scale tensor as a row-major numpy array."""
+    a = t.cpu().numpy()
+    return unpack_k64(a) if pack == api.PACK_K64 else a
+
+
 def quant_both(x: torch.Tensor, amax_held: float, layout: str, rnd: int = 0, T: float = 448.0,
                seed: int = 0, subseq: int = 0, transposed: bool = False, ld_pad: int = 0,
-               block: int = 16, scale_fmt: int = 0):
+               block: int = 16, scale_fmt: int = 0, pack: int = 0):
     """Quantize the CPU tensor x on the GPU and with the oracle.
 
     Returns (gpu dict of numpy arrays, oracle Quantized). ld_pad > 0 stores x
-    on the device inside a wider buffer (row stride cols + ld_pad)."""
+    on the device inside a wider buffer (row stride cols + ld_pad). pack
+    selects the GPU outputs' packing; the numpy arrays are row-major either
+    way (K64 outputs are unpacked by index permutation only)."""
     lay_g, lay_o = LAYOUTS[layout]
     if ld_pad:
         buf = torch.zeros((x.shape[0], x.shape[1] + ld_pad), dtype=x.dtype)
@@ -39,13 +54,14 @@ def quant_both(x: torch.Tensor, amax_held: float, layout: str, rnd: int = 0, T: 
     else:
         xd = x.to(DEV)
     q, qt, diag = api.quantize(xd, dev_scalar(amax_held), T, lay_g, rnd, seed, subseq,
-                               transposed=transposed, with_diag=True, block=block, scale_fmt=scale_fmt)
+                               transposed=transposed, with_diag=True, block=block, scale_fmt=scale_fmt,
+                               pack=pack)
     torch.cuda.synchronize()
-    g = dict(codes=q.codes.cpu().numpy(), scales=q.scales.cpu().numpy(),
+    g = dict(codes=host_rows(q.codes, pack), scales=host_rows(q.scales, pack),
              S=q.enc_scale.cpu().numpy()[0], diag=diag.cpu().numpy(), q=q, qt=qt)
     if qt is not None:
-        g["codes_t"] = qt.codes.cpu().numpy()
-        g["scales_t"] = qt.scales.cpu().numpy()
+        g["codes_t"] = host_rows(qt.codes, pack)
+        g["scales_t"] = host_rows(qt.scales, pack)
     o = oracle.quantize(host_view(x), amax_held, T, lay_o, rnd, seed, subseq, transposed=transposed,
                         block=block, scale_fmt=scale_fmt)
     if layout == "row16" and transposed:

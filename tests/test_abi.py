@@ -28,14 +28,15 @@ def test_library_exports_every_declared_function():
     assert set(names) == set(_lib.EXPORTS), names
     for n in names:
         assert hasattr(L, n), n
-    assert L.fp4q_abi_version() == 2
+    assert L.fp4q_abi_version() == 3
     for s in range(7):
         assert L.fp4q_status_str(s)
 
 
-def q(rows, cols, layout=_lib.ROW16, codes=FAKE, scales=FAKE, S=FAKE, block=16, fmt=_lib.UE5M3):
+def q(rows, cols, layout=_lib.ROW16, codes=FAKE, scales=FAKE, S=FAKE, block=16, fmt=_lib.UE5M3,
+      pack=_lib.PACK_ROWS):
     return _lib.QTensorC(codes.value if codes else None, scales.value if scales else None,
-                         S.value if S else None, rows, cols, layout, block, fmt)
+                         S.value if S else None, rows, cols, layout, block, fmt, pack)
 
 
 def quant(**kw):
@@ -126,13 +127,35 @@ def test_format_validation():
 
     def qf(rows=64, cols=64, layout=_lib.ROW16, block=32, fmt=_lib.E4M3, ct=None, st=None):
         return L.fp4q_quantize_fmt(FAKE, _lib.BF16, rows, cols, cols, FAKE, 448.0, layout, block, fmt,
-                                   _lib.RNE, 0, 0, FAKE, FAKE, None, ct, st, None, None)
+                                   _lib.PACK_ROWS, _lib.RNE, 0, 0, FAKE, FAKE, None, ct, st, None, None)
     assert qf(block=24) == _lib.E_ARG
     assert qf(fmt=3) == _lib.E_ARG
     assert qf(cols=48) == _lib.E_SHAPE                       # ROW blocks of 32
     assert qf(rows=48, layout=_lib.COL16) == _lib.E_SHAPE    # COL blocks of 32
     assert qf(rows=48, layout=_lib.TILE16x16) == _lib.E_SHAPE
     assert qf(rows=48, ct=FAKE, st=FAKE) == _lib.E_SHAPE     # ROW + COL needs rows % 32
+
+
+def test_packing_validation():
+    L = _lib.lib()
+
+    def qp(rows=128, cols=128, layout=_lib.ROW16, pack=_lib.PACK_K64, ct=None, st=None):
+        return L.fp4q_quantize_fmt(FAKE, _lib.BF16, rows, cols, cols, FAKE, 448.0, layout, 16, _lib.UE5M3,
+                                   pack, _lib.RNE, 0, 0, FAKE, FAKE, None, ct, st, None, None)
+    assert qp(pack=2) == _lib.E_ARG
+    assert qp(pack=-1) == _lib.E_ARG
+    # K64 needs every output's contraction length to be a multiple of 64
+    assert qp(cols=96) == _lib.E_SHAPE                                  # ROW16: cols
+    assert qp(cols=96, layout=_lib.TILE16x16) == _lib.E_SHAPE           # TILE: cols
+    assert qp(rows=96, layout=_lib.COL16) == _lib.E_SHAPE               # COL16: rows
+    assert qp(rows=96, ct=FAKE, st=FAKE) == _lib.E_SHAPE                # ROW16 + COL16: rows too
+    assert qp(rows=96, layout=_lib.TILE16x16, ct=FAKE, st=FAKE) == _lib.E_SHAPE  # transposed tile copy
+    # operands: K64 needs cols % 64; the two GEMM operands must share the packing
+    k = _lib.PACK_K64
+    assert L.fp4q_dequant(q(32, 96, pack=k), FAKE, _lib.F32, None) == _lib.E_SHAPE
+    assert L.fp4q_dequant(q(32, 64, pack=3), FAKE, _lib.F32, None) == _lib.E_ARG
+    assert L.fp4q_linear_fwd(q(32, 64, pack=k), q(48, 64), FAKE, _lib.BF16, None) == _lib.E_ARG
+    assert L.fp4q_linear_wgrad(q(32, 96, pack=k), q(48, 96, pack=k), FAKE, _lib.F32, None) == _lib.E_SHAPE
 
 
 def test_oversized_grids_are_rejected():

@@ -157,3 +157,23 @@ def test_inference_measures_weight_amax_once():
     xq = oracle.quantize(inputs.bf16_bits(x), float(oracle.amax(inputs.bf16_bits(x))), **kw).q
     wq = oracle.quantize(w4, aw0, layout=oracle.TILE16).q
     close(y, oracle.gemm(xq, wq), "inference fwd")
+
+
+@pytest.mark.parametrize("m,k,n", [(96, 80, 48), (128, 192, 320)])
+def test_packing_follows_the_shapes(m, k, n):
+    # K64 wherever every contraction length (K, N, M) is a multiple of 64,
+    # row-major otherwise; the results match the oracle either way
+    rng = np.random.default_rng(m + k + n)
+    x = torch.from_numpy(inputs.activation(rng, m, k, inputs.outlier_columns(rng, k))).to(torch.bfloat16)
+    w = torch.from_numpy(inputs.gaussian(rng, n, k, 0.02))
+    dy = torch.from_numpy(inputs.loguniform_grad(rng, m, n)).to(torch.bfloat16)
+    r = Fp4Recipe(seed=4)
+    layer = FP4Linear(k, n, r, device=DEV)
+    with torch.no_grad():
+        layer.weight.copy_(w.to(DEV))
+    y, dx, dw = run(layer, x, dy)
+    A = [float(oracle.amax(v)) for v in (inputs.bf16_bits(x), w.numpy(), inputs.bf16_bits(dy))]
+    ry, rdx, rdw = oracle_step(x, w, dy, *A, r, subseq=0)
+    close(y, ry, "fwd")
+    close(dx, rdx, "dgrad")
+    close(dw, rdw, "wgrad")

@@ -7,13 +7,16 @@ representable values; too few random bits can bias it), "Rounding in
 Preconditioner Space ..." App. A.2 Definition 5 (SR probabilities; inputs on
 a level stay; inputs outside the range go to the nearer endpoint).
 
-Pins: the published Philox known-answer vectors; brute-force unbiasedness
+Pins: the published Philox known-answer vectors; rocRAND's own
+implementation of the generator (its state engine compiled for the host);
+brute-force unbiasedness
 over many independent words; adjacency and fixed points; layout independence
 of the per-element word.
 """
 import os
 
 import numpy as np
+import pytest
 
 import oracle
 
@@ -127,3 +130,43 @@ def test_sr_region_origin_matches_whole_tensor():
     colp = oracle.quantize(np.ascontiguousarray(x[16:48, 8:24]), a, rnd=oracle.SR, seed=3,
                            layout=oracle.COL16, origin=(16, 8, 64)).q
     assert np.array_equal(colp.codes, colw.codes[8:24, 8:24])
+
+
+def _rocrand_words():
+    """Build (once) and return the path of the host program that prints
+    rocRAND's Philox4x32-10 words (tests/rocrand_philox_words.cpp)."""
+    import shutil
+    import subprocess
+    src = os.path.join(os.path.dirname(__file__), "rocrand_philox_words.cpp")
+    hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(hipcc) or not os.path.exists("/opt/rocm/include/rocrand/rocrand_kernel.h"):
+        pytest.skip("hipcc or the rocRAND headers are not installed")
+    out_dir = os.path.join(os.path.dirname(__file__), "_build")
+    os.makedirs(out_dir, exist_ok=True)
+    exe = os.path.join(out_dir, "rocrand_philox_words")
+    if not os.path.exists(exe) or os.path.getmtime(exe) < os.path.getmtime(src):
+        subprocess.run([hipcc, "-O1", "-o", exe, src], check=True, capture_output=True, timeout=300)
+    return exe
+
+
+def test_philox_words_match_rocrand():
+    # rocRAND's Philox4x32-10, an implementation independent of the oracle's
+    # (same published generator): rocrand_init(seed, subsequence, offset)
+    # keys the generator with the 64-bit seed and starts at counter
+    # (offset / 4 as 64 bits, subsequence as 64 bits), returning word
+    # offset % 4 -- the oracle's per-element word with subsequence < 2^32
+    import subprocess
+    exe = _rocrand_words()
+    rng = np.random.default_rng(17)
+    cases = [(0, 0, i) for i in range(8)]
+    cases += [(int(s), int(q), int(i)) for s, q, i in zip(rng.integers(0, 2 ** 63, 200, dtype=np.uint64),
+                                                            rng.integers(0, 2 ** 32, 200, dtype=np.uint64),
+                                                            rng.integers(0, 2 ** 40, 200, dtype=np.uint64))]
+    # the low counter word wrapping into the high one
+    cases += [(0x1234_5678_9ABC_DEF0, 3, 4 * (2 ** 32 - 1) + k) for k in range(8)]
+    cases += [(2 ** 64 - 1, 2 ** 32 - 1, 2 ** 35 + 1)]
+    stdin = "".join(f"{s} {q} {i}\n" for s, q, i in cases)
+    res = subprocess.run([exe], input=stdin, capture_output=True, text=True, check=True, timeout=60)
+    got = [int(t) for t in res.stdout.split()]
+    want = [int(oracle.sr_word(s, q, i)) for s, q, i in cases]
+    assert got == want

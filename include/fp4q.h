@@ -217,7 +217,10 @@ fp4q_status fp4q_linear_wgrad(const fp4q_qtensor *dyqt, const fp4q_qtensor *xqt,
  * W's transposed copy, X COL16), contiguous along K as for the other calls.
  * For each output the contraction is cut into consecutive 64-wide slices of
  * K; each slice's dot product of the decoded operands is formed with fp32
- * MFMA accumulation (exact whenever the slice sum is representable); the
+ * MFMA accumulation (exact when the slice's partial sums are representable
+ * in the MFMA's internal precision, as when its products span a few
+ * binades; measured otherwise within about 2 units in the last place of the
+ * largest product of each 16-product group, not correctly rounded); the
  * slice sums are added in slice order with fp32 additions rounded toward
  * zero; if snap_log2 > 0 the sum is rounded to the nearest multiple of
  * 2^-snap_log2 (ties to even; 10 gives the page's 1/1024 grid); then

@@ -137,3 +137,26 @@ def test_dequant_k64_equals_rows(block, fmt):
         (qr, _, _), (qk, _, _) = _pair(x, held(x), layout, block=block, fmt=fmt)
         for dt in (torch.float32, torch.bfloat16):
             assert torch.equal(api.dequant(qr, dt), api.dequant(qk, dt))
+
+
+def test_k64_empty_shapes():
+    # no rows, or a contraction of length 0 (a multiple of 64): nothing is
+    # written but the tensor scale, and a K = 0 GEMM writes zeros
+    a = torch.tensor([3.0], dtype=torch.float32, device=DEV)
+    for shape in ((0, 128), (64, 0)):
+        x = torch.zeros(shape, dtype=torch.bfloat16, device=DEV)
+        for layout in (api.ROW16, api.COL16, api.TILE16x16):
+            if layout == api.COL16 and shape[0] % 64:
+                continue
+            q, _, _ = api.quantize(x, a, layout=layout, pack=K64)
+            torch.cuda.synchronize()
+            assert q.codes.numel() == 0 and q.scales.numel() == 0
+            assert float(q.enc_scale.cpu()[0]) == np.float32(np.float32(6 * 448.0) / np.float32(3.0))
+    xa = torch.zeros((32, 0), dtype=torch.bfloat16, device=DEV)
+    xb = torch.zeros((48, 0), dtype=torch.bfloat16, device=DEV)
+    qa, _, _ = api.quantize(xa, a, pack=K64)
+    qb, _, _ = api.quantize(xb, a, layout=api.TILE16x16, pack=K64)
+    y = torch.full((32, 48), float("nan"), dtype=torch.float32, device=DEV)
+    api.fp4q_linear_fwd(qa, qb, y)
+    torch.cuda.synchronize()
+    assert torch.all(y == 0)

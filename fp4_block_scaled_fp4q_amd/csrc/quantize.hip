@@ -353,8 +353,11 @@ __global__ __launch_bounds__(kDualThreads<kBlk>()) void quant_dual_kernel(
   if (diag) add_diag(diag, nzero, nsat);
 }
 
-template <bool kBF16>
-constexpr int sub_tiles() { return kBF16 ? 4 : 2; }
+// 16-row tile rows per lane: two (32 rows, 16 contiguous transposed bytes
+// per column) measured faster than four for bf16 inputs, whose smaller grid
+// left too few waves per SIMD to keep the loads in flight. Even, since
+// store_col_codes writes 16-byte pieces.
+constexpr int kTileSub = 2;
 
 // Stores the 8 * kSub bytes of one column's codes (nsub sub-tiles valid),
 // as 16-byte pieces when the column row is 16-byte aligned.
@@ -383,7 +386,7 @@ __global__ __launch_bounds__(kThreads) void quant_tile_kernel(
     uint8_t* __restrict__ codes_t, uint8_t* __restrict__ scales_t, float* __restrict__ enc_out,
     int32_t* __restrict__ diag) {
   constexpr int es = kBF16 ? 2 : 4;
-  constexpr int kSub = sub_tiles<kBF16>();
+  constexpr int kSub = kTileSub;
   const int item = xcd_order(blockIdx.x, col_groups * row_groups);
   const int cg = item / row_groups;
   const int rg = item - cg * row_groups;
@@ -553,7 +556,7 @@ hipError_t launch_typed(const QuantArgs& a, hipStream_t s) {
                            a.enc_scale_out, a.diag);
       return hipGetLastError();
     }
-    constexpr int ksub = sub_tiles<kBF16>();
+    constexpr int ksub = kTileSub;
     const int row_groups = (int)((a.rows / 16 + ksub - 1) / ksub);
     const dim3 grid((uint32_t)(col_groups * row_groups));
     if (a.codes_t)

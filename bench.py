@@ -12,6 +12,7 @@ step of sample-and-hold tensor scaling:
   Y  = Xq Wq^T     (bf16 out)    fwd
   dX = dYq Wq      (bf16 out)    dgrad
   dW = dYq^T Xq    (fp32 out)    wgrad
+Quantized operands use the K64 packing (--pack rows: row-major).
 value = 3 * 2 M N K flops / step time (TFLOP/s); inputs are resident in HBM
 before timing starts. Also measured in the same run: each kernel's average
 duration inside the step (HIP events on the launch stream), the quantize-only workload

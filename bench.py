@@ -3,13 +3,14 @@
 
 One step = the whole hot path on the FFN up-projection shape
 (X 16384x4096 bf16, W 14336x4096 bf16, dY 16384x14336 bf16), as a refresh
-step of sample-and-hold tensor scaling:
-  amax(X), amax(W), amax(dY)
+step of sample-and-hold tensor scaling, in training order:
+  amax(X), amax(W)
   quantize X  ROW16 + COL16 RNE (fwd operand; wgrad operand along tokens), one pass
   quantize W  TILE16x16 RNE + transposed copy (fwd and dgrad operand)
+  Y  = Xq Wq^T     (bf16 out)    fwd
+  amax(dY)
   quantize dY ROW16 + COL16 SR  (dgrad operand; wgrad operand along tokens), one
               pass, one Philox word per element for both
-  Y  = Xq Wq^T     (bf16 out)    fwd
   dX = dYq Wq      (bf16 out)    dgrad
   dW = dYq^T Xq    (fp32 out)    wgrad
 Quantized operands use the K64 packing (--pack rows: row-major).
@@ -100,11 +101,11 @@ def main():
     T = 448.0
     seed = 0
 
-    # every launch of one step, in order, as (kernel family, callable)
+    # every launch of one step, in the order of a training step (forward,
+    # then the backward once dY exists), as (kernel family, callable)
     ops = [
         ("amax", lambda: api.fp4q_amax(X, amax["X"])),
         ("amax", lambda: api.fp4q_amax(W, amax["W"])),
-        ("amax", lambda: api.fp4q_amax(dY, amax["dY"])),
         # X: ROW16 (fwd) and COL16 (wgrad) in one pass
         ("quant_x_row_col", lambda: api.fp4q_quantize_fmt(X, amax["X"], T, api.ROW16, 16, api.UE5M3, pack,
                                                           api.RNE, 0, 0, xq.codes, xq.scales, S["x"],
@@ -112,11 +113,12 @@ def main():
         ("quant_w_tile", lambda: api.fp4q_quantize_fmt(W, amax["W"], T, api.TILE16x16, 16, api.UE5M3, pack,
                                                        api.RNE, 0, 0, wq.codes, wq.scales, S["w"],
                                                        wqt.codes, wqt.scales)),
+        ("gemm_fwd", lambda: api.fp4q_linear_fwd(xq, wq, Y)),
+        ("amax", lambda: api.fp4q_amax(dY, amax["dY"])),
         # dY: ROW16 (dgrad) and COL16 (wgrad) in one pass, one Philox word per element
         ("quant_dy_row_col_sr", lambda: api.fp4q_quantize_fmt(dY, amax["dY"], T, api.ROW16, 16, api.UE5M3,
                                                               pack, api.SR, seed, 0, dyq.codes, dyq.scales,
                                                               S["dy"], dyqt.codes, dyqt.scales)),
-        ("gemm_fwd", lambda: api.fp4q_linear_fwd(xq, wq, Y)),
         ("gemm_dgrad", lambda: api.fp4q_linear_dgrad(dyq, wqt, dX)),
         ("gemm_wgrad", lambda: api.fp4q_linear_wgrad(dyqt, xqt, dW)),
     ]

@@ -299,14 +299,18 @@ def main():
         log(args, f"variant {tag}: quantize-only {v_us:.2f} us, fwd GEMM {f_us:.1f} us")
     del Xrot
 
-    # traffic from committed rocprofv3 counters, valid only for this source
+    # traffic from committed rocprofv3 counters, valid only for this GEMM
+    # source built with these flags
     traffic = None
     tf = os.path.join(ROOT, "profiles", "gemm_ffn_up_traffic.json")
     if os.path.exists(tf):
         try:
             rec = json.load(open(tf))
-            src = open(os.path.join(ROOT, "fp4_block_scaled_fp4q_amd", "csrc", "gemm.hip"), "rb").read()
-            if rec.get("gemm_hip_sha256") == hashlib.sha256(src).hexdigest():
+            pkg = os.path.join(ROOT, "fp4_block_scaled_fp4q_amd")
+            src = open(os.path.join(pkg, "csrc", "gemm.hip"), "rb").read()
+            flags = open(os.path.join(pkg, "build.py"), "rb").read()
+            if (rec.get("gemm_hip_sha256") == hashlib.sha256(src).hexdigest()
+                    and rec.get("build_py_sha256") == hashlib.sha256(flags).hexdigest()):
                 traffic = rec.get("bytes_per_launch")
         except Exception:
             traffic = None

@@ -67,9 +67,10 @@ typedef enum {
  * 0x00..0x7E: 2^-9 .. 448, the same code's UE5M3 value times 256). */
 typedef enum { FP4Q_UE5M3 = 0, FP4Q_E4M3 = 1 } fp4q_scale_fmt;
 
-/* Memory packing of an operand's codes and scales. The pages fix what is
- * stored (E2M1 codes two per byte, element 2j in bits 3:0 and 2j+1 in bits
- * 7:4 of byte j of a row; one scale byte per block), not where it lives.
+/* Memory packing of an operand's codes and scales. The pages fix what a
+ * code and a scale are, not where they live. Within a row this library
+ * stores two E2M1 codes per byte (element 2j in bits 3:0 and 2j+1 in bits
+ * 7:4 of byte j) and one scale byte per block, in either packing:
  *  FP4Q_PACK_ROWS: row-major, as the shapes in fp4q_layout give them.
  *  FP4Q_PACK_K64: the contraction axis cut into tiles of 64 elements; tile t
  *    holds every row's 32 code bytes back to back, then the next tile:

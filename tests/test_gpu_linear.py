@@ -115,6 +115,48 @@ def test_gemm_deterministic_and_launch_independent():
     assert torch.equal(y3, y1[128:256])
 
 
+@pytest.mark.parametrize("M,N,K,out,pack", [
+    (8292, 4144, 128, torch.float32, api.PACK_ROWS),  # 561 tiles, edge tiles
+    (8292, 4144, 192, torch.bfloat16, api.PACK_K64),
+    (8192, 4096, 64, torch.bfloat16, api.PACK_ROWS),  # 512 tiles
+])
+def test_gemm_many_tiles(M, N, K, out, pack):
+    # More 256 x 256 output tiles than compute units, a tile count that does
+    # not divide evenly over the eight XCD ranges, and partial edge tiles:
+    # the whole output is within the GEMM bound of the oracle, and every
+    # tile equals what a launch over a 256-row slice of A computes for it,
+    # bit for bit (a tile's result does not depend on its position in the
+    # launch).
+    rng = np.random.default_rng(M + N + K)
+    A = torch.from_numpy(inputs.activation(rng, M, K, inputs.outlier_columns(rng, K)))
+    B = torch.from_numpy(inputs.gaussian(rng, N, K, 0.02))
+    ga, oa = quant_both(A, float(oracle.amax(host_view(A))), "row16", pack=pack)
+    gb, ob = quant_both(B, float(oracle.amax(host_view(B))), "tile", pack=pack)
+    assert_quant_equal(ga, oa)
+    assert_quant_equal(gb, ob)
+    y = torch.full((M, N), float("nan"), dtype=out, device=DEV)
+    api.fp4q_linear_fwd(ga["q"], gb["q"], y)
+    torch.cuda.synchronize()
+    _gemm_check(y, oracle.gemm(oa.q, ob.q))
+    if pack == api.PACK_K64:
+        # the same product from row-major operands, bit for bit
+        ra, _ = quant_both(A, float(oracle.amax(host_view(A))), "row16")
+        rb, _ = quant_both(B, float(oracle.amax(host_view(B))), "tile")
+        yr = torch.full((M, N), float("nan"), dtype=out, device=DEV)
+        api.fp4q_linear_fwd(ra["q"], rb["q"], yr)
+        torch.cuda.synchronize()
+        assert torch.equal(y, yr)
+        return
+    qa = ga["q"]
+    for r0 in (0, 256 * 17, (M // 256) * 256):
+        rows = min(256, M - r0)
+        sub = api.QTensor(qa.codes[r0:r0 + rows], qa.scales[r0:r0 + rows], qa.enc_scale, rows, K, api.ROW16)
+        ys = torch.full((rows, N), float("nan"), dtype=out, device=DEV)
+        api.fp4q_linear_fwd(sub, gb["q"], ys)
+        torch.cuda.synchronize()
+        assert torch.equal(ys, y[r0:r0 + rows]), r0
+
+
 @pytest.mark.parametrize("M,N,K", [(512, 1024, 1024), (500, 1000, 1040), (2048, 1024, 512)])
 def test_split_tail_fp32_gemm(M, N, K):
     # fp32 outputs whose tile count leaves the last round of workgroups at

@@ -4,9 +4,10 @@
 One step = the whole hot path on the FFN up-projection shape
 (X 16384x4096 bf16, W 14336x4096 bf16, dY 16384x14336 bf16), as a refresh
 step of sample-and-hold tensor scaling, in training order:
-  amax(X), amax(W)
-  quantize X  ROW16 + COL16 RNE (fwd operand; wgrad operand along tokens), one pass
-  quantize W  TILE16x16 RNE + transposed copy (fwd and dgrad operand)
+  amax(X), then quantize X  ROW16 + COL16 RNE (fwd operand; wgrad operand
+              along tokens), one pass
+  amax(W), then quantize W  TILE16x16 RNE + transposed copy (fwd and dgrad
+              operand)
   Y  = Xq Wq^T     (bf16 out)    fwd
   amax(dY)
   quantize dY ROW16 + COL16 SR  (dgrad operand; wgrad operand along tokens), one
@@ -103,13 +104,15 @@ def main():
 
     # every launch of one step, in the order of a training step (forward,
     # then the backward once dY exists), as (kernel family, callable)
+    # each operand's amax is followed by its own quantization (which then
+    # re-reads a tensor that the amax has just streamed through the cache)
     ops = [
         ("amax", lambda: api.fp4q_amax(X, amax["X"])),
-        ("amax", lambda: api.fp4q_amax(W, amax["W"])),
         # X: ROW16 (fwd) and COL16 (wgrad) in one pass
         ("quant_x_row_col", lambda: api.fp4q_quantize_fmt(X, amax["X"], T, api.ROW16, 16, api.UE5M3, pack,
                                                           api.RNE, 0, 0, xq.codes, xq.scales, S["x"],
                                                           xqt.codes, xqt.scales)),
+        ("amax", lambda: api.fp4q_amax(W, amax["W"])),
         ("quant_w_tile", lambda: api.fp4q_quantize_fmt(W, amax["W"], T, api.TILE16x16, 16, api.UE5M3, pack,
                                                        api.RNE, 0, 0, wq.codes, wq.scales, S["w"],
                                                        wqt.codes, wqt.scales)),

@@ -94,20 +94,22 @@ class _Fp4LinearFn(torch.autograd.Function):
         x2 = x.reshape(-1, x.shape[-1])
         if not x2.is_contiguous():
             x2 = x2.contiguous()
-        ax = st.amax_x.update(x2, refresh)
-        if training or not st.weight_measured:
-            aw = st.amax_w.update(weight, refresh)
-            st.weight_measured = True
-        else:
-            aw = st.amax_w.value  # inference: the weight's amax is measured once
         M, K, N = x2.shape[0], x2.shape[1], weight.shape[0]
         # every contraction the packing must serve: K (fwd), and with a
         # backward N (dgrad) and M (wgrad)
         lengths = (K, N, M) if need_grad else (K,)
         pack = api.PACK_K64 if r.pack == api.PACK_K64 and all(n % 64 == 0 for n in lengths) else api.PACK_ROWS
         kw = dict(block=r.block, scale_fmt=r.scale_fmt, pack=pack)
+        # each operand's amax is followed by its own quantization, which then
+        # re-reads a tensor the amax has just streamed through the cache
+        ax = st.amax_x.update(x2, refresh)
         # X: ROW (fwd) and, when a backward follows, COL (wgrad) in one pass
         xq, xqt, _ = api.quantize(x2, ax, r.target, api.ROW16, api.RNE, transposed=need_grad, **kw)
+        if training or not st.weight_measured:
+            aw = st.amax_w.update(weight, refresh)
+            st.weight_measured = True
+        else:
+            aw = st.amax_w.value  # inference: the weight's amax is measured once
         wq, wqt, _ = api.quantize(weight, aw, r.target, api.TILE16x16, api.RNE, transposed=need_grad,
                                   **kw)
         y = torch.empty((x2.shape[0], weight.shape[0]), dtype=torch.bfloat16, device=x.device)

@@ -230,6 +230,13 @@ __device__ __forceinline__ uint32_t seg_word(const RowSeg& g, int c) {
   }
 }
 
+// Workgroup barrier for the LDS double buffer: waits for this wave's LDS
+// (and scalar) operations only. __syncthreads() would also wait for every
+// global load in flight, i.e. for the codes prefetched for later k tiles,
+// on every k tile. The memory clobber keeps the compiler from moving memory
+// operations across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // LDS slot of 16-byte chunk c of tile row r (8 chunks per 128-byte row).
 template <int kSwz>
 __device__ __forceinline__ int slot(int r, int c) {
@@ -378,13 +385,16 @@ __global__ __launch_bounds__(64 * kWavesM * kWavesN) void gemm_kernel(
     for (int j = 0; j < kFN; ++j) bfr[j] = __builtin_bit_cast(bf16x8, buf[slot<kSwz>(brow0 + 32 * j, ch)]);
   };
 
-  for (int kt = k_begin; kt < nk; ++kt) {
+  // one k tile: MFMAs on the current buffer while the codes of tile kt + 1
+  // (gd) are decoded into the other one and those of tile kt + 2 are loaded
+  // into gl. The loop runs two k tiles per trip with gd and gl swapping
+  // roles, so no register copy waits for the loads just issued.
+  auto k_step = [&](int kt, const RowSeg* gd, RowSeg* gl) {
     constexpr int kBuf = (kBM + kBN) * row_pitch<kSwz>();
     const uint4* cur_buf = lds + ((kt - k_begin) & 1) * kBuf;
     uint4* next_buf = lds + ((kt - k_begin + 1) & 1) * kBuf;
     // codes of tile kt + 2 (the last tile again near the end: harmless)
-    RowSeg ng[kRows];
-    load_rows(ng, (int64_t)min(kt + 2, nk - 1) * BK);
+    load_rows(gl, (int64_t)min(kt + 2, nk - 1) * BK);
     bf16x8 af[2][kFM], bfr[2][kFN];
     load_frags(cur_buf, 0, af[0], bfr[0]);
 #pragma unroll
@@ -408,7 +418,7 @@ __global__ __launch_bounds__(64 * kWavesM * kWavesN) void gemm_kernel(
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                 af[cb][i], bfr[cb][j], (kProbe && s == 0) ? f32x16{} : acc[i][j], 0, 0, 0);
         }
-        decode_piece(next_buf, g, s, p);
+        decode_piece(next_buf, gd, s, p);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -430,10 +440,15 @@ __global__ __launch_bounds__(64 * kWavesM * kWavesN) void gemm_kernel(
       __builtin_amdgcn_s_setreg(kModeRound32, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
-#pragma unroll
-    for (int i = 0; i < kRows; ++i) g[i] = ng[i];
-    __syncthreads();
+    lds_barrier();
+  };
+  RowSeg g2[kRows];
+  int kt = k_begin;
+  for (; kt + 1 < nk; kt += 2) {
+    k_step(kt, g, g2);
+    k_step(kt + 1, g2, g);
   }
+  if (kt < nk) k_step(kt, g, g2);
   if constexpr (kProbe) {
 #pragma unroll
     for (int i = 0; i < kFM; ++i)

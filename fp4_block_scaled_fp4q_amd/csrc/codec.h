@@ -51,6 +51,14 @@ __device__ __forceinline__ uint4 load_nt16(const void* p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// Workgroup barrier for data exchanged through LDS: waits for this wave's
+// LDS (and scalar memory) operations only, then s_barrier. __syncthreads()
+// also waits for every global load and store still in flight (prefetches
+// for later work, output stores), which these kernels never need to order
+// against another wave. The memory clobber keeps the compiler from moving
+// memory operations across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // Nearest UE5M3 code of raw >= 0 with ties to the even code, then repair:
 // a code that rounds to 0 becomes 0x01, one that rounds beyond 61,440
 // (raw >= 63,488, the midpoint to 2^16, tie to the even side) becomes 0xF7.

@@ -230,13 +230,6 @@ __device__ __forceinline__ uint32_t seg_word(const RowSeg& g, int c) {
   }
 }
 
-// Workgroup barrier for the LDS double buffer: waits for this wave's LDS
-// (and scalar) operations only. __syncthreads() would also wait for every
-// global load in flight, i.e. for the codes prefetched for later k tiles,
-// on every k tile. The memory clobber keeps the compiler from moving memory
-// operations across it.
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-
 // LDS slot of 16-byte chunk c of tile row r (8 chunks per 128-byte row).
 template <int kSwz>
 __device__ __forceinline__ int slot(int r, int c) {
@@ -368,7 +361,7 @@ __global__ __launch_bounds__(64 * kWavesM * kWavesN) void gemm_kernel(
 #pragma unroll
       for (int p = 0; p < kPieces; ++p) decode_piece(lds, g, s, p);
     load_rows(g, (int64_t)min(k_begin + 1, nk - 1) * BK);
-    __syncthreads();
+    lds_barrier();  // the codes just requested are first needed by a decode of the first k tile
   }
 
   const int arow0 = wm * kTM + (lane & 31);
@@ -388,7 +381,9 @@ __global__ __launch_bounds__(64 * kWavesM * kWavesN) void gemm_kernel(
   // one k tile: MFMAs on the current buffer while the codes of tile kt + 1
   // (gd) are decoded into the other one and those of tile kt + 2 are loaded
   // into gl. The loop runs two k tiles per trip with gd and gl swapping
-  // roles, so no register copy waits for the loads just issued.
+  // roles, so no register copy waits for the loads just issued, and the
+  // barrier between k tiles (lds_barrier) waits for LDS traffic only, not
+  // for the codes in flight for later k tiles.
   auto k_step = [&](int kt, const RowSeg* gd, RowSeg* gl) {
     constexpr int kBuf = (kBM + kBN) * row_pitch<kSwz>();
     const uint4* cur_buf = lds + ((kt - k_begin) & 1) * kBuf;

@@ -308,7 +308,7 @@ __global__ __launch_bounds__(kDualThreads<kBlk>()) void quant_dual_kernel(
       for (int k = 0; k < kBlk / 4; ++k) dw[k] = make_uint4(w[4 * k], w[4 * k + 1], w[4 * k + 2], w[4 * k + 3]);
     }
   }
-  __syncthreads();
+  lds_barrier();  // phase 2 reads LDS only; the ROW code stores may still be in flight
 
   // ---- phase 2: one column block per thread
   {

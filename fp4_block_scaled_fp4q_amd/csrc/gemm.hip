@@ -41,6 +41,13 @@
 #include "codec.h"
 #include "kernels.h"
 
+#ifndef FP4Q_GEMM_SWZ
+#define FP4Q_GEMM_SWZ 2
+#endif
+#ifndef FP4Q_GEMM_ROTATE
+#define FP4Q_GEMM_ROTATE 1
+#endif
+
 namespace fp4q {
 namespace {
 
@@ -384,26 +391,41 @@ __global__ __launch_bounds__(64 * kWavesM * kWavesN) void gemm_kernel(
   // roles, so no register copy waits for the loads just issued, and the
   // barrier between k tiles (lds_barrier) waits for LDS traffic only, not
   // for the codes in flight for later k tiles.
+  // Fragments of the current and the next k16 step. With FP4Q_GEMM_ROTATE
+  // the decode of the next buffer ends with the third k16 step, the barrier
+  // comes before the fourth, and the next k tile's first fragments are read
+  // while the fourth step's MFMAs run (they are in registers when that k
+  // tile starts).
+  bf16x8 af[2][kFM], bfr[2][kFN];
+  if (FP4Q_GEMM_ROTATE && nk > k_begin) load_frags(lds, 0, af[0], bfr[0]);
+  constexpr int kMfma = kFM * kFN;                   // MFMAs per k16 step
+  constexpr int kDecStride = kMfma >= 8 ? kMfma / 4 : 1;
   auto k_step = [&](int kt, const RowSeg* gd, RowSeg* gl) {
     constexpr int kBuf = (kBM + kBN) * row_pitch<kSwz>();
     const uint4* cur_buf = lds + ((kt - k_begin) & 1) * kBuf;
     uint4* next_buf = lds + ((kt - k_begin + 1) & 1) * kBuf;
     // codes of tile kt + 2 (the last tile again near the end: harmless)
     load_rows(gl, (int64_t)min(kt + 2, nk - 1) * BK);
-    bf16x8 af[2][kFM], bfr[2][kFN];
-    load_frags(cur_buf, 0, af[0], bfr[0]);
+    if (!FP4Q_GEMM_ROTATE) load_frags(cur_buf, 0, af[0], bfr[0]);
 #pragma unroll
     for (int s = 0; s < BK / 16; ++s) {
       const int cb = s & 1;
-      if (s + 1 < BK / 16) load_frags(cur_buf, s + 1, af[cb ^ 1], bfr[cb ^ 1]);
-      // block s of the next tile is decoded in kPieces pieces, each after
-      // kMfmaPerPiece MFMAs, so that the VALU work issues while the matrix
-      // core is busy
+      if (s + 1 < BK / 16) {
+        load_frags(cur_buf, s + 1, af[cb ^ 1], bfr[cb ^ 1]);
+      } else if (FP4Q_GEMM_ROTATE) {
+        // every wave's decode into next_buf and its reads of this step's
+        // fragments are done: the next k tile's first fragments can be read
+        lds_barrier();
+        load_frags(next_buf, 0, af[cb ^ 1], bfr[cb ^ 1]);
+      }
+      if (FP4Q_GEMM_ROTATE) {
+        // the 2 * (BK / 16) decode pieces of the next buffer over the first
+        // three k16 steps (3, 3, 2), each after kDecStride MFMAs
+        constexpr int kQ = 2 * (BK / 16);
+        const int q0 = s == 0 ? 0 : s == 1 ? 3 : s == 2 ? 6 : kQ;
+        const int q1 = s == 0 ? 3 : s == 1 ? 6 : kQ;
 #pragma unroll
-      for (int p = 0; p < kPieces; ++p) {
-#pragma unroll
-        for (int u = 0; u < kMfmaPerPiece; ++u) {
-          const int f = p * kMfmaPerPiece + u;
+        for (int f = 0; f < kMfma; ++f) {
           const int i = f / kFN, j = f % kFN;
           if constexpr (kF16)
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, af[cb][i]),
@@ -412,9 +434,34 @@ __global__ __launch_bounds__(64 * kWavesM * kWavesN) void gemm_kernel(
           else
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                 af[cb][i], bfr[cb][j], (kProbe && s == 0) ? f32x16{} : acc[i][j], 0, 0, 0);
+          const int q = q0 + f / kDecStride;
+          if ((f + 1) % kDecStride == 0 && q < q1) {
+            decode_piece(next_buf, gd, q >> 1, q & 1);
+            __builtin_amdgcn_sched_barrier(0);
+          }
         }
-        decode_piece(next_buf, gd, s, p);
         __builtin_amdgcn_sched_barrier(0);
+      } else {
+        // block s of the next tile is decoded in kPieces pieces, each after
+        // kMfmaPerPiece MFMAs, so that the VALU work issues while the matrix
+        // core is busy
+#pragma unroll
+        for (int p = 0; p < kPieces; ++p) {
+#pragma unroll
+          for (int u = 0; u < kMfmaPerPiece; ++u) {
+            const int f = p * kMfmaPerPiece + u;
+            const int i = f / kFN, j = f % kFN;
+            if constexpr (kF16)
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, af[cb][i]),
+                                                                 __builtin_bit_cast(f16x8, bfr[cb][j]),
+                                                                 acc[i][j], 0, 0, 0);
+            else
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                  af[cb][i], bfr[cb][j], (kProbe && s == 0) ? f32x16{} : acc[i][j], 0, 0, 0);
+          }
+          decode_piece(next_buf, gd, s, p);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
     }
     if constexpr (kProbe) {
@@ -435,7 +482,7 @@ __global__ __launch_bounds__(64 * kWavesM * kWavesN) void gemm_kernel(
       __builtin_amdgcn_s_setreg(kModeRound32, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
-    lds_barrier();
+    if (!FP4Q_GEMM_ROTATE) lds_barrier();
   };
   RowSeg g2[kRows];
   int kt = k_begin;
@@ -556,9 +603,6 @@ __global__ __launch_bounds__(256) void zero_split_tiles(float* __restrict__ y, i
 #endif
 #ifndef FP4Q_GEMM_WAVES_N
 #define FP4Q_GEMM_WAVES_N 4
-#endif
-#ifndef FP4Q_GEMM_SWZ
-#define FP4Q_GEMM_SWZ 2
 #endif
 
 namespace {

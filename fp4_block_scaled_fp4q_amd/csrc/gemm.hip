@@ -400,12 +400,17 @@ __global__ __launch_bounds__(64 * kWavesM * kWavesN) void gemm_kernel(
   if (FP4Q_GEMM_ROTATE && nk > k_begin) load_frags(lds, 0, af[0], bfr[0]);
   constexpr int kMfma = kFM * kFN;                   // MFMAs per k16 step
   constexpr int kDecStride = kMfma >= 8 ? kMfma / 4 : 1;
+  // the rotated schedule's 3 + 3 + 2 decode pieces: one tile row per thread
+  static_assert(!FP4Q_GEMM_ROTATE || (kRows == 1 && BK == 64), "rotated k tile: one decoded row per thread");
   auto k_step = [&](int kt, const RowSeg* gd, RowSeg* gl) {
     constexpr int kBuf = (kBM + kBN) * row_pitch<kSwz>();
     const uint4* cur_buf = lds + ((kt - k_begin) & 1) * kBuf;
     uint4* next_buf = lds + ((kt - k_begin + 1) & 1) * kBuf;
-    // codes of tile kt + 2 (the last tile again near the end: harmless)
-    load_rows(gl, (int64_t)min(kt + 2, nk - 1) * BK);
+    // codes of tile kt + 2 (the last tile again near the end: harmless);
+    // in the rotated default kernel they are requested after the first MFMA,
+    // so that their address arithmetic issues under it
+    constexpr bool kLateLoad = FP4Q_GEMM_ROTATE && !kProbe;
+    if (!kLateLoad) load_rows(gl, (int64_t)min(kt + 2, nk - 1) * BK);
     if (!FP4Q_GEMM_ROTATE) load_frags(cur_buf, 0, af[0], bfr[0]);
 #pragma unroll
     for (int s = 0; s < BK / 16; ++s) {
@@ -437,6 +442,10 @@ __global__ __launch_bounds__(64 * kWavesM * kWavesN) void gemm_kernel(
           const int q = q0 + f / kDecStride;
           if ((f + 1) % kDecStride == 0 && q < q1) {
             decode_piece(next_buf, gd, q >> 1, q & 1);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+          if (kLateLoad && s == 0 && f == 0) {
+            load_rows(gl, (int64_t)min(kt + 2, nk - 1) * BK);
             __builtin_amdgcn_sched_barrier(0);
           }
         }

@@ -20,6 +20,10 @@
 //    [A tile; B tile] into LDS, double buffered, in pieces placed between
 //    the MFMAs that consume the other buffer. Decoding once per workgroup
 //    costs (256 + 256) * 64 elements per 256 * 256 * 64 MACs.
+//  * The k tile is rotated: the decode ends with the third of its four k16
+//    steps, the workgroup barrier (LDS traffic only, so the codes in flight
+//    for later tiles are not waited for) comes before the fourth, and the
+//    next tile's first fragments are read under the fourth step's MFMAs.
 //  * Decode: v_cvt_scalef32_pk_f16_fp4 (scale 1.0) gives two exact E2M1
 //    values as halves and one packed half multiply by the block's scale pair
 //    forms the products: two instructions per pair of elements. (The bf16

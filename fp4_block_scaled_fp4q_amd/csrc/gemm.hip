@@ -7,8 +7,11 @@
 // [2^-18, 368640]. The default accumulation decodes it times 2^-5, which is
 // exact in binary16 (at most 11520, a multiple of 2^-23), and contracts on
 // v_mfma_f32_32x32x16_f16 with fp32 accumulation; alpha absorbs the 2^10.
-// The probe-matched mode decodes to bf16 (exact as well) and contracts on
-// v_mfma_f32_32x32x16_bf16.
+// The probe-matched mode uses the same binary16 operands (each of its
+// 64-wide slice sums, their toward-zero additions and its snap then see
+// the values times 2^-10 exactly: no rounding step here depends on a power
+// of two scaling); FP4Q_PROBE_F16=0 builds it with a bf16 decode on
+// v_mfma_f32_32x32x16_bf16 instead.
 //
 // Design (gfx950):
 //  * A workgroup owns a 256 x 256 output tile; its 8 waves (2 along M x 4
@@ -50,6 +53,9 @@
 #endif
 #ifndef FP4Q_GEMM_ROTATE
 #define FP4Q_GEMM_ROTATE 1
+#endif
+#ifndef FP4Q_PROBE_F16
+#define FP4Q_PROBE_F16 1
 #endif
 
 namespace fp4q {
@@ -281,9 +287,9 @@ __global__ __launch_bounds__(64 * kWavesM * kWavesN) void gemm_kernel(
   constexpr int kPieces = 2 * kRows;          // decode8 calls per thread per k16 step
   constexpr int kMfmaPerPiece = kFM * kFN / kPieces;
   static_assert(kFM * kFN % kPieces == 0, "MFMA count must split evenly");
-  // operands decoded to binary16 (times 2^-5) for the default accumulation;
-  // the probe mode keeps bf16
-  constexpr bool kF16 = !kProbe;
+  // operands decoded to binary16 (times 2^-5); a bf16 decode for the probe
+  // mode if FP4Q_PROBE_F16 is 0
+  constexpr bool kF16 = !kProbe || FP4Q_PROBE_F16;
 
   // 2 buffers x (A tile + B tile) = 128 KiB
   extern __shared__ uint4 lds[];
@@ -379,8 +385,8 @@ __global__ __launch_bounds__(64 * kWavesM * kWavesN) void gemm_kernel(
   const int brow0 = kBM + wn * kTN + (lane & 31);
   const int hi = lane >> 5;
 
-  // fragments: eight 16-bit values per lane (binary16 in the default mode,
-  // bf16 in the probe mode), bit-cast to the MFMA's operand type
+  // fragments: eight 16-bit values per lane (binary16, or bf16 for a probe
+  // mode built with FP4Q_PROBE_F16=0), bit-cast to the MFMA's operand type
   auto load_frags = [&](const uint4* buf, int s, bf16x8* af, bf16x8* bfr) {
     const int ch = 2 * s + hi;
 #pragma unroll
@@ -439,7 +445,7 @@ __global__ __launch_bounds__(64 * kWavesM * kWavesN) void gemm_kernel(
           if constexpr (kF16)
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, af[cb][i]),
                                                                __builtin_bit_cast(f16x8, bfr[cb][j]),
-                                                               acc[i][j], 0, 0, 0);
+                                                               (kProbe && s == 0) ? f32x16{} : acc[i][j], 0, 0, 0);
           else
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                 af[cb][i], bfr[cb][j], (kProbe && s == 0) ? f32x16{} : acc[i][j], 0, 0, 0);
@@ -467,7 +473,7 @@ __global__ __launch_bounds__(64 * kWavesM * kWavesN) void gemm_kernel(
             if constexpr (kF16)
               acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, af[cb][i]),
                                                                  __builtin_bit_cast(f16x8, bfr[cb][j]),
-                                                                 acc[i][j], 0, 0, 0);
+                                                                 (kProbe && s == 0) ? f32x16{} : acc[i][j], 0, 0, 0);
             else
               acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                   af[cb][i], bfr[cb][j], (kProbe && s == 0) ? f32x16{} : acc[i][j], 0, 0, 0);
@@ -505,6 +511,9 @@ __global__ __launch_bounds__(64 * kWavesM * kWavesN) void gemm_kernel(
   }
   if (kt < nk) k_step(kt, g, g2);
   if constexpr (kProbe) {
+    // sums of binary16 operands carry 2^-10 (alpha restores it): the snap
+    // grid moves by the same 10 bits
+    constexpr int kSnapShift = kF16 ? 10 : 0;
 #pragma unroll
     for (int i = 0; i < kFM; ++i)
 #pragma unroll
@@ -513,7 +522,8 @@ __global__ __launch_bounds__(64 * kWavesM * kWavesN) void gemm_kernel(
         for (int e = 0; e < 16; ++e) {
           const float t = tot[i][j][e];
           acc[i][j][e] = snap_log2 > 0
-                             ? __builtin_ldexpf(__builtin_rintf(__builtin_ldexpf(t, snap_log2)), -snap_log2)
+                             ? __builtin_ldexpf(__builtin_rintf(__builtin_ldexpf(t, snap_log2 + kSnapShift)),
+                                                -snap_log2 - kSnapShift)
                              : t;
         }
   }

@@ -344,6 +344,9 @@ def main():
                      "achieved": round(gemm_tflops, 2), "peak": MFMA16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(gemm_tflops / MFMA16_PEAK_TFLOPS, 4), "traffic": traffic},
         "kernels_us": {k: round(v, 2) for k, v in kern.items()},
+        # each GEMM's achieved rate as a fraction of the dense fp16/bf16 MFMA peak
+        "gemm_frac": {g: round(2.0 * M * N * K / (kern["gemm_" + g] * 1e-6) / 1e12 / MFMA16_PEAK_TFLOPS, 4)
+                      for g in ("fwd", "dgrad", "wgrad")},
         "codec_gbs": {k: round(v, 1) for k, v in codec_gbs.items()},
         "quantize_only": {"workload": "8192x4096 bf16 ROW16 RNE, held amax", "us": round(q_us, 2),
                           "GB/s": round(q_gbs, 1), "frac_hbm": round(q_gbs / HBM_PEAK_GBS, 4)},

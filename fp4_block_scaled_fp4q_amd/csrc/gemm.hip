@@ -29,9 +29,9 @@
 //    next tile's first fragments are read under the fourth step's MFMAs.
 //  * Decode: v_cvt_scalef32_pk_f16_fp4 (scale 1.0) gives two exact E2M1
 //    values as halves and one packed half multiply by the block's scale pair
-//    forms the products: two instructions per pair of elements. (The bf16
-//    decode of the probe mode takes four: a conversion to fp32, two fp32
-//    multiplies and a packing conversion.)
+//    forms the products: two instructions per pair of elements. (A bf16
+//    decode, kept for FP4Q_PROBE_F16=0, takes four: a conversion to fp32,
+//    two fp32 multiplies and a packing conversion.)
 //  * LDS rows are 8 chunks of 16 bytes (8 k each) at a 144-byte pitch, so
 //    any 16 consecutive rows fall on distinct banks for the fragment reads
 //    (32 rows, one chunk) and the row-wise decode writes.
@@ -264,8 +264,9 @@ constexpr int row_pitch() { return kSwz == 2 ? kChunks + 1 : kChunks; }
 // slice result is added to a running sum with binary32 additions rounded
 // toward zero (the MODE register's single-precision rounding field is set
 // to round-toward-zero around those additions only); the epilogue
-// optionally snaps the sum to multiples of 2^-snap_log2 (ties to even)
-// before applying alpha.
+// optionally snaps the sum to multiples of 2^-snap_log2 (ties to even; on
+// the 2^-10-scaled binary16 sums, multiples of 2^-(snap_log2 + 10)) before
+// applying alpha.
 template <int kBM, int kBN, bool kFullK, bool kF32Out, int kWavesM, int kWavesN, int kSwz, bool kProbe,
           bool kFmt, bool kK64>
 __global__ __launch_bounds__(64 * kWavesM * kWavesN) void gemm_kernel(

@@ -48,6 +48,11 @@
 #include "codec.h"
 #include "kernels.h"
 
+// Build switches, defaults measured fastest. FP4Q_GEMM_SWZ: LDS layout of
+// the decoded tiles (2: 144-byte padded row pitch; 0 and 1: 128-byte rows
+// with the 16-byte chunk index XORed by row bits). FP4Q_GEMM_ROTATE: the
+// rotated k tile described above (0: decode, barrier, then all four k16
+// steps). FP4Q_PROBE_F16: binary16 operands in the probe-matched mode.
 #ifndef FP4Q_GEMM_SWZ
 #define FP4Q_GEMM_SWZ 2
 #endif

@@ -70,6 +70,7 @@ fp4q_status gemm(const fp4q_qtensor* a, const fp4q_qtensor* b, void* y, fp4q_dty
   if (a->cols != b->cols) return FP4Q_E_SHAPE;
   if (a->pack != b->pack) return FP4Q_E_ARG;
   if (a->rows > 0 && b->rows > 0 && !y) return FP4Q_E_NULL;
+  if (y && !aligned(y, es)) return FP4Q_E_ALIGN;  // element stores and fp32 atomic adds
   const int64_t tm = (a->rows + 127) / 128, tn = (b->rows + 127) / 128;
   if (tm > 0 && tn > (0x7FFFFFFF / 512) / tm) return FP4Q_E_SHAPE;
   if (probe)

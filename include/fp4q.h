@@ -201,7 +201,8 @@ fp4q_status fp4q_dequant(const fp4q_qtensor *q, void *out, fp4q_dtype ot, void *
  * a multiple of 16 and of each operand's block size) and `rows` a multiple of
  * the block size when their layout is TILE. The two operands may use
  * different block sizes and scale formats; they must share the packing
- * (FP4Q_E_ARG otherwise).
+ * (FP4Q_E_ARG otherwise). The output (device) is aligned to its element
+ * size (FP4Q_E_ALIGN otherwise).
  */
 fp4q_status fp4q_linear_fwd(const fp4q_qtensor *xq, const fp4q_qtensor *wq, void *y,
                             fp4q_dtype yt, void *stream);
@@ -226,7 +227,8 @@ fp4q_status fp4q_linear_wgrad(const fp4q_qtensor *dyqt, const fp4q_qtensor *xqt,
  * zero; if snap_log2 > 0 the sum is rounded to the nearest multiple of
  * 2^-snap_log2 (ties to even; 10 gives the page's 1/1024 grid); then
  * y = RN_out(RN(sum * alpha)), alpha = 1 / (Sa Sb) as in the calls above.
- * snap_log2 in [0, 30]; yt FP4Q_F32 or FP4Q_BF16.
+ * snap_log2 in [0, 30]; yt FP4Q_F32 or FP4Q_BF16; y aligned to its element
+ * size.
  */
 fp4q_status fp4q_linear_probe(const fp4q_qtensor *a, const fp4q_qtensor *b, void *y,
                               fp4q_dtype yt, int32_t snap_log2, void *stream);

@@ -95,6 +95,8 @@ def test_gemm_and_dequant_validation():
         assert fn(a, q(48, 64, 5), FAKE, _lib.BF16, None) == _lib.E_ARG
         assert fn(a, q(48, 64, _lib.COL16), FAKE, _lib.BF16, None) == _lib.E_ARG
         assert fn(a, b, None, _lib.BF16, None) == _lib.E_NULL
+        assert fn(a, b, ctypes.c_void_p(0x10001), _lib.BF16, None) == _lib.E_ALIGN
+        assert fn(a, b, ctypes.c_void_p(0x10002), _lib.F32, None) == _lib.E_ALIGN
         assert fn(q(32, 64, S=None), b, FAKE, _lib.BF16, None) == _lib.E_NULL
         assert fn(q(32, 64, codes=FAKE_ODD), b, FAKE, _lib.BF16, None) == _lib.E_ALIGN
         assert fn(a, q(48, 64, _lib.TILE16x16, scales=ctypes.c_void_p(0x10002)), FAKE, _lib.BF16,
@@ -113,6 +115,7 @@ def test_probe_gemm_validation():
     assert L.fp4q_linear_probe(a, q(48, 80, _lib.TILE16x16), FAKE, _lib.F32, 10, None) == _lib.E_SHAPE
     assert L.fp4q_linear_probe(a, b, FAKE, 7, 10, None) == _lib.E_DTYPE
     assert L.fp4q_linear_probe(a, b, None, _lib.BF16, 10, None) == _lib.E_NULL
+    assert L.fp4q_linear_probe(a, b, ctypes.c_void_p(0x10002), _lib.F32, 10, None) == _lib.E_ALIGN
 
 
 def test_format_validation():

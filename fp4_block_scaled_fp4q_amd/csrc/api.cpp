@@ -134,6 +134,7 @@ fp4q_status fp4q_quantize_fmt(const void* x, fp4q_dtype xt, int64_t rows, int64_
   // ROW with the second orientation also needs whole column blocks
   if (codes_t && layout == FP4Q_ROW16 && rows % block) return FP4Q_E_SHAPE;
   if (!amax_held) return FP4Q_E_NULL;
+  if (!aligned(amax_held, 4)) return FP4Q_E_ALIGN;
   if (!dims_ok(rows, cols) || !dims_ok(rows, ld) || ld < cols) return FP4Q_E_SHAPE;
   if (layout != FP4Q_COL16 && cols % block) return FP4Q_E_SHAPE;
   if (layout != FP4Q_ROW16 && rows % block) return FP4Q_E_SHAPE;

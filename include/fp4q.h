@@ -121,11 +121,11 @@ fp4q_status fp4q_amax(const void *x, fp4q_dtype xt, int64_t rows, int64_t cols, 
 /*
  * Quantize x ([rows, cols], dtype xt, row stride ld) to E2M1 codes with UE5M3
  * block scales (§3-§5 of the page).
- *  amax_held (device, one fp32): the held tensor amax A. The tensor scale is
- *    S = RN(RN(6 * target) / A), S = 1 if A is 0 or not finite, and the
- *    largest finite fp32 if the quotient overflows; target is the UE5M3
- *    target T of §5.2 (448 default; finite and > 0). S is written to
- *    *enc_scale_out (device, optional).
+ *  amax_held (device, one fp32, 4-byte aligned): the held tensor amax A.
+ *    The tensor scale is S = RN(RN(6 * target) / A), S = 1 if A is 0 or not
+ *    finite, and the largest finite fp32 if the quotient overflows; target
+ *    is the UE5M3 target T of §5.2 (448 default; finite and > 0). S is
+ *    written to *enc_scale_out (device, optional).
  *  Per block: bamax = max |x|; if 0, scale code 0 and sign-only codes. Else
  *    raw = RN(RN(bamax / 6) * S), scale = nearest UE5M3 (ties to even), with
  *    repair: a scale rounding to 0 becomes 0x01, one rounding above 61440

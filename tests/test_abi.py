@@ -71,6 +71,7 @@ def test_quantize_validation():
     assert quant(x=FAKE_ODD) == _lib.E_ALIGN
     assert quant(ld=68) == _lib.E_ALIGN                       # 136-byte bf16 rows
     assert quant(codes=FAKE_ODD) == _lib.E_ALIGN
+    assert quant(amax=ctypes.c_void_p(0x10002)) == _lib.E_ALIGN
 
 
 def test_amax_validation():

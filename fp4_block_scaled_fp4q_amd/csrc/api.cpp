@@ -150,17 +150,21 @@ fp4q_status fp4q_quantize_fmt(const void* x, fp4q_dtype xt, int64_t rows, int64_
     if (!x || !codes || !scales) return FP4Q_E_NULL;
     if (!aligned(x, 16) || (ld * es) % 16) return FP4Q_E_ALIGN;
     if (!aligned(codes, 8) || (codes_t && !aligned(codes_t, 8))) return FP4Q_E_ALIGN;
-    // workgroup counts of the kernels (see the launchers)
-    int64_t groups;
+    // workgroup counts (upper bounds) and sizes of the kernels, as the
+    // launchers set them up: a launch stays below 2^31 threads
+    int64_t groups, threads;
     if (layout == FP4Q_ROW16 && !codes_t) {
       groups = rows * ((cols / block + 63) / 64);
+      threads = 64;
     } else if (layout == FP4Q_TILE16x16) {
       groups = ((cols / 8 + 255) / 256) * (rows / 16);
+      threads = 256;
     } else {
       const int64_t tc = 1024 / block, tr = 4 * block;
       groups = ((cols + tc - 1) / tc) * ((rows + tr - 1) / tr);
+      threads = 4 * tc;
     }
-    if (groups > kMaxGridX) return FP4Q_E_SHAPE;
+    if (groups > 0x7FFFFFFF / threads) return FP4Q_E_SHAPE;
   }
   if ((enc_scale_out && !aligned(enc_scale_out, 4)) || (diag && !aligned(diag, 4)))
     return FP4Q_E_ALIGN;

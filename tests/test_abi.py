@@ -173,6 +173,10 @@ def test_oversized_grids_are_rejected():
                            0, FAKE, FAKE, None, None, None, None, None) == _lib.E_SHAPE
     assert L.fp4q_quantize(FAKE, _lib.BF16, huge, 4096, 4096, FAKE, 448.0, _lib.COL16, _lib.RNE, 0, 0,
                            FAKE, FAKE, None, None, None, None, None) == _lib.E_SHAPE
+    # ROW16 alone: one 64-lane workgroup per 64 blocks of a row, so 2^25 rows
+    # of 64 columns are one workgroup past 2^31 threads
+    assert L.fp4q_quantize(FAKE, _lib.BF16, 1 << 25, 64, 64, FAKE, 448.0, _lib.ROW16, _lib.RNE, 0, 0,
+                           FAKE, FAKE, None, None, None, None, None) == _lib.E_SHAPE
     assert L.fp4q_linear_fwd(q(huge, 64), q(huge, 64), FAKE, _lib.F32, None) == _lib.E_SHAPE
     assert L.fp4q_dequant(q(huge, 4096), FAKE, _lib.F32, None) == _lib.E_SHAPE
     # negative sizes

@@ -226,3 +226,32 @@ def test_gemm_extreme_scale_codes(case, out):
         # sum, so fp32 accumulation leaves only a tiny relative error
         assert rel_fro(yf, round_out(ref, out)) <= (2e-5 if out == torch.float32 else GEMM_TOL)
     _gemm_check(y, ref)
+
+
+@pytest.mark.parametrize("out,N", [(torch.float32, (1 << 22) + 48), (torch.bfloat16, (1 << 23) + 48)])
+def test_gemm_output_beyond_4gib(out, N):
+    # An output of 5 GB: every 256-row tile band spans more than 2^32 bytes,
+    # so interior tiles take the 64-bit-offset store path, and the fp32 case
+    # also runs its last tiles as split K halves. Sampled columns (the first
+    # and last tiles among them) match the oracle, and no output element is
+    # left unwritten. With a held amax, ROW16 codes of a row depend on that
+    # row alone, so the oracle quantizes only the sampled rows of B.
+    M, K = 300, 64
+    rng = np.random.default_rng(N)
+    A = torch.from_numpy(inputs.activation(rng, M, K, inputs.outlier_columns(rng, K)))
+    B = inputs.gaussian(rng, N, K, 0.02)
+    aa, ab = float(oracle.amax(host_view(A))), float(np.abs(B).max())
+    ga, oa = quant_both(A, aa, "row16")
+    assert_quant_equal(ga, oa)
+    qb = api.quantize(torch.from_numpy(B).to(DEV), dev_scalar(ab))[0]
+    y = torch.full((M, N), float("nan"), dtype=out, device=DEV)
+    api.fp4q_linear_fwd(ga["q"], qb, y)
+    torch.cuda.synchronize()
+    assert not torch.isnan(y).any().item()
+    cols = np.unique(np.concatenate([np.arange(0, 300), np.arange(N - 300, N),
+                                     rng.choice(N, 256, replace=False)]))
+    ob = oracle.quantize(B[cols], ab, 448.0, oracle.ROW16, 0, 0, 0)
+    idx = torch.from_numpy(cols).to(DEV)
+    np.testing.assert_array_equal(qb.codes.index_select(0, idx).cpu().numpy(), ob.q.codes)
+    np.testing.assert_array_equal(qb.scales.index_select(0, idx).cpu().numpy(), ob.q.scales)
+    _gemm_check(y.index_select(1, idx), oracle.gemm(oa.q, ob.q))

@@ -151,11 +151,13 @@ def test_inference_measures_weight_amax_once():
             y = layer(x.to(DEV))
         torch.cuda.synchronize()
     assert float(layer.held_amax()["w"].cpu()[0]) == aw0
-    # the output uses the held weight amax (the scaled weight under the old S)
-    kw = {}
+    # the held weight amax is the first weight's; the output uses it (the
+    # scaled weight under the old S)
+    aw_oracle = float(oracle.amax(w.numpy()))
+    assert aw0 == aw_oracle
     w4 = (w * 4.0).numpy()
-    xq = oracle.quantize(inputs.bf16_bits(x), float(oracle.amax(inputs.bf16_bits(x))), **kw).q
-    wq = oracle.quantize(w4, aw0, layout=oracle.TILE16).q
+    xq = oracle.quantize(inputs.bf16_bits(x), float(oracle.amax(inputs.bf16_bits(x)))).q
+    wq = oracle.quantize(w4, aw_oracle, layout=oracle.TILE16).q
     close(y, oracle.gemm(xq, wq), "inference fwd")
 
 

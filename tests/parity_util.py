@@ -3,6 +3,9 @@
 same seeded host inputs, and compare."""
 from __future__ import annotations
 
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import torch
 
@@ -99,3 +102,95 @@ def round_out(y: np.ndarray, dtype: torch.dtype) -> np.ndarray:
 
 
 GEMM_TOL = 2e-3
+
+
+# ---------------------------------------------------------------- large cases
+def _workers() -> int:
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def oracle_quantize_par(x: np.ndarray, amax_held: float, layout: int, rnd: int = 0, T: float = 448.0,
+                        seed: int = 0, subseq: int = 0, transposed: bool = False, chunk: int = 512):
+    """oracle.quantize of a large tensor, run as independent chunks on host
+    threads (the oracle's C calls release the GIL). Under a held amax a ROW16
+    (or TILE) row band and a COL16 column band depend on their own elements
+    only, and SR takes the chunk's origin in the whole tensor, so the
+    concatenated chunks equal one call on the whole tensor. Returns
+    (q, qt) oracle QTensors; qt is the TILE transposed copy when asked."""
+    rows, cols = x.shape
+    col = layout == oracle.COL16
+    n = cols if col else rows
+    starts = list(range(0, n, chunk))
+
+    def run(s):
+        e = min(n, s + chunk)
+        part = np.ascontiguousarray(x[:, s:e] if col else x[s:e])
+        origin = (0, s, cols) if col else (s, 0, cols)
+        return oracle.quantize(part, amax_held, T, layout, rnd, seed, subseq, transposed=transposed,
+                               origin=origin)
+
+    with ThreadPoolExecutor(_workers()) as ex:
+        parts = list(ex.map(run, starts))
+    S = parts[0].q.S
+    codes = np.concatenate([p.q.codes for p in parts], axis=0)
+    if layout == oracle.TILE16:
+        scales = np.concatenate([p.q.scales for p in parts], axis=0)
+        q = oracle.QTensor(codes, scales, S, rows, cols, oracle.TILE16)
+        qt = None
+        if transposed:
+            qt = oracle.QTensor(np.concatenate([p.qt.codes for p in parts], axis=1),
+                                np.concatenate([p.qt.scales for p in parts], axis=1), S, cols, rows,
+                                oracle.TILE16)
+        return q, qt
+    scales = np.concatenate([p.q.scales for p in parts], axis=0)
+    if col:
+        return oracle.QTensor(codes, scales, S, cols, rows, oracle.ROW16), None
+    return oracle.QTensor(codes, scales, S, rows, cols, oracle.ROW16), None
+
+
+def sub_operand(q: oracle.QTensor, r0: int, n: int) -> oracle.QTensor:
+    """Rows [r0, r0+n) of an oracle operand (n and r0 multiples of 16 for TILE)."""
+    if q.layout == oracle.TILE16:
+        return oracle.QTensor(q.codes[r0:r0 + n], q.scales[r0 // 16:(r0 + n) // 16], q.S, n, q.cols,
+                              q.layout)
+    return oracle.QTensor(q.codes[r0:r0 + n], q.scales[r0:r0 + n], q.S, n, q.cols, q.layout)
+
+
+def gemm_ref_and_bound(a: oracle.QTensor, b: oracle.QTensor, out: torch.dtype):
+    """The oracle's contraction (fp64) and an elementwise bound on what an
+    fp32-accumulated evaluation of it may differ by:
+        2 K 2^-24 (|A| |B|^T) / (Sa Sb)   (at most K - 1 fp32 roundings of
+                                            partial sums, each within 2^-24
+                                            of a partial sum of |products|;
+                                            doubled for the matrix core's
+                                            grouped additions)
+      + 2^-22 |Y|                          (alpha's rounding and the fp32 product)
+      + for bf16 outputs, 2^-8 of the fp32 value (RNE to 8 significant bits).
+    |A| |B|^T is taken in fp64 from the oracle's exactly decoded operands."""
+    A = oracle.decode_f64(a)
+    B = oracle.decode_f64(b)
+    s = np.float64(a.S) * np.float64(b.S)
+    ref = (A @ B.T) / s
+    absp = (np.abs(A) @ np.abs(B).T) / s
+    del A, B
+    K = a.cols
+    bound = 2.0 * K * 2.0 ** -24 * absp + 2.0 ** -22 * np.abs(ref) + 1e-37
+    if out == torch.bfloat16:
+        bound += 2.0 ** -8 * (np.abs(ref) + bound)
+    return ref, bound
+
+
+def check_gemm_elementwise(got: torch.Tensor, ref: np.ndarray, bound: np.ndarray, what: str):
+    """Every element within its bound, and the 2e-3 relative Frobenius bar
+    against RN_out of the fp64 reference."""
+    g = got.float().cpu().numpy().astype(np.float64)
+    assert np.isfinite(g).all(), f"{what}: non-finite output"
+    err = np.abs(g - ref)
+    bad = err > bound
+    if bad.any():
+        i = np.argwhere(bad)[0]
+        raise AssertionError(f"{what}: {int(bad.sum())} elements beyond the bound, first at {tuple(i)}: "
+                             f"got {g[tuple(i)]!r}, ref {ref[tuple(i)]!r}, bound {bound[tuple(i)]!r}")
+    fro = rel_fro(g, round_out(ref, got.dtype))
+    assert fro <= GEMM_TOL, f"{what}: rel Frobenius {fro:.3e}"
+    return fro

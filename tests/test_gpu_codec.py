@@ -220,3 +220,76 @@ def test_input_beyond_4gib():
                                       err_msg=str(b))
         np.testing.assert_array_equal(qs.codes[b:b + 16].cpu().numpy(), o_sr.q.codes, err_msg=str(b))
         np.testing.assert_array_equal(qs.scales[b:b + 16].cpu().numpy(), o_sr.q.scales, err_msg=str(b))
+
+
+def _fp32_neighbourhoods(span: int) -> np.ndarray:
+    """Every binary32 value within +-span units in the last place of each
+    E2M1 level (0, 0.5, 1, 1.5, 2, 3, 4, 6) and of each rounding midpoint
+    between levels (0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5), both signs."""
+    pts = [0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0, 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0]
+    d = np.arange(-span, span + 1, dtype=np.int64)
+    bits = [np.arange(0, span + 1, dtype=np.int64)]  # 0 and the smallest subnormals
+    for p in pts:
+        bits.append(int(np.float32(p).view(np.uint32)) + d)
+    u = np.unique(np.concatenate(bits)).astype(np.uint32)
+    return np.concatenate([u, u | np.uint32(0x80000000)]).view(np.float32)
+
+
+def _latin_anchor_tensor(vals: np.ndarray, cols: int) -> torch.Tensor:
+    """An fp32 tensor whose every 16-element row block and every 16-row column
+    block holds exactly one 6.0 (at column 16 j + r % 16 of row r), the other
+    positions filled with vals in order (then zeros). With held amax 6 and
+    T = 448, S = 448 and every block (row, column or 16 x 16 tile) has bamax
+    within 0.6% of 6, so its scale is 448 and r = RN(S / dec) = 1: the payload
+    rule sees each value itself."""
+    per_row = cols - cols // 16
+    rows = -(-len(vals) // per_row)
+    rows = -(-rows // 64) * 64
+    x = np.zeros((rows, cols), np.float32)
+    anchor = np.zeros((rows, cols), bool)
+    r = np.arange(rows)[:, None]
+    anchor[r, 16 * np.arange(cols // 16)[None, :] + (r % 16)] = True
+    body = np.zeros(rows * per_row, np.float32)
+    body[:len(vals)] = vals
+    x[anchor] = 6.0
+    x[~anchor] = body
+    return torch.from_numpy(x)
+
+
+@pytest.mark.parametrize("layout", ["row16", "row16+col16", "tile"])
+@pytest.mark.parametrize("rnd", [0, 1])
+def test_fp32_payload_neighbourhoods(layout, rnd):
+    # fp32 inputs with full 24-bit significands: each E2M1 level and each
+    # midpoint between levels +-2^16 ulps (and the subnormals next to zero),
+    # through the ROW16 kernel, the one-pass ROW16 + COL16 kernel and the
+    # 16 x 16 tile kernel, RNE and SR, bit-exact against the oracle. The
+    # hardware RNE conversion and the stochastic-rounding threshold are
+    # thereby checked where a wrong tie rule or a lost low bit would show.
+    x = _latin_anchor_tensor(_fp32_neighbourhoods(1 << 16), 1024)
+    both = layout == "row16+col16"
+    g, o = quant_both(x, 6.0, "row16" if both else layout, rnd, 448.0, seed=0xC0FFEE, subseq=9,
+                      transposed=(both or layout == "tile"))
+    assert g["S"] == np.float32(448.0)
+    assert (o.q.scales == 0xBE).all()
+    assert_quant_equal(g, o, f"{layout} rnd={rnd}")
+
+
+@pytest.mark.parametrize("layout", ["row16", "row16+col16", "tile"])
+def test_sr_decision_boundaries(layout):
+    # every element exactly at the last value that rounds down or the first
+    # that rounds up for its own Philox word (tests/sr_threshold.py), in every
+    # E2M1 interval, through the ROW16, one-pass ROW16 + COL16 and tile
+    # kernels: bit-exact against the oracle. A word conversion or threshold
+    # off by one unit anywhere flips codes here.
+    from sr_threshold import threshold_tensor
+    seed, subseq = 0x1234_5678_9ABC, 11
+    x, want = threshold_tensor(128, 512, seed, subseq)
+    both = layout == "row16+col16"
+    g, o = quant_both(torch.from_numpy(x), 6.0, "row16" if both else layout, 1, 448.0, seed=seed,
+                      subseq=subseq, transposed=(both or layout == "tile"))
+    if layout != "tile":
+        codes = np.zeros(x.shape, np.int64)
+        codes[:, 0::2] = o.q.codes & 0xF
+        codes[:, 1::2] = o.q.codes >> 4
+        np.testing.assert_array_equal(codes & 7, want)
+    assert_quant_equal(g, o, layout)

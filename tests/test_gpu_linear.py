@@ -231,8 +231,8 @@ def test_gemm_extreme_scale_codes(case, out):
 @pytest.mark.parametrize("out,N", [(torch.float32, (1 << 22) + 48), (torch.bfloat16, (1 << 23) + 48)])
 def test_gemm_output_beyond_4gib(out, N):
     # An output of 5 GB: every 256-row tile band spans more than 2^32 bytes,
-    # so interior tiles take the 64-bit-offset store path, and the fp32 case
-    # also runs its last tiles as split K halves. Sampled columns (the first
+    # so interior tiles take the 64-bit-offset store path (K = 64 is one k
+    # tile, so no tile is split into K halves here). Sampled columns (the first
     # and last tiles among them) match the oracle, and no output element is
     # left unwritten. With a held amax, ROW16 codes of a row depend on that
     # row alone, so the oracle quantizes only the sampled rows of B.

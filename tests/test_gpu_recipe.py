@@ -179,3 +179,35 @@ def test_packing_follows_the_shapes(m, k, n):
     close(y, ry, "fwd")
     close(dx, rdx, "dgrad")
     close(dw, rdw, "wgrad")
+
+
+def test_fp32_activations_and_gradients_quantized_directly():
+    # fp32 X gives an fp32 output, so autograd hands the backward an fp32
+    # dY, which reaches the quantizer as it is: all three outputs (fp32)
+    # lie within the elementwise fp32-accumulation bound of the oracle's
+    # contraction of its own quantizations of the fp32 tensors (a bf16
+    # rounding of dY before its stochastic rounding moves codes by far more
+    # than that bound)
+    from parity_util import check_gemm_elementwise, gemm_ref_and_bound
+    rng = np.random.default_rng(11)
+    x = torch.from_numpy(inputs.activation(rng, M, K, inputs.outlier_columns(rng, K)))
+    w = torch.from_numpy(inputs.gaussian(rng, N, K, 0.02))
+    dy = torch.from_numpy(inputs.loguniform_grad(rng, M, N))
+    r = Fp4Recipe(seed=9)
+    layer = FP4Linear(K, N, r, device=DEV)
+    with torch.no_grad():
+        layer.weight.copy_(w.to(DEV))
+    y, dx, dw = run(layer, x, dy)
+    assert y.dtype == torch.float32 and dx.dtype == torch.float32 and dw.dtype == torch.float32
+    A = [float(oracle.amax(v.numpy())) for v in (x, w, dy)]
+    xq = oracle.quantize(x.numpy(), A[0], r.target, oracle.ROW16).q
+    xqt = oracle.quantize(x.numpy(), A[0], r.target, oracle.COL16).q
+    wq = oracle.quantize(w.numpy(), A[1], r.target, oracle.TILE16, transposed=True)
+    dyq = oracle.quantize(dy.numpy(), A[2], r.target, oracle.ROW16, oracle.SR, r.seed, 0).q
+    dyqt = oracle.quantize(dy.numpy(), A[2], r.target, oracle.COL16, oracle.SR, r.seed, 0).q
+    ref, bound = gemm_ref_and_bound(xq, wq.q, torch.float32)
+    check_gemm_elementwise(y, ref, bound, "fwd")
+    ref, bound = gemm_ref_and_bound(dyq, wq.qt, torch.float32)
+    check_gemm_elementwise(dx, ref, bound, "dgrad")
+    ref, bound = gemm_ref_and_bound(dyqt, xqt, torch.float32)
+    check_gemm_elementwise(dw, ref, bound, "wgrad")

@@ -170,3 +170,19 @@ def test_philox_words_match_rocrand():
     got = [int(t) for t in res.stdout.split()]
     want = [int(oracle.sr_word(s, q, i)) for s, q, i in cases]
     assert got == want
+
+
+def test_sr_decision_boundaries_per_word():
+    # every element at the last value that rounds down or the first that
+    # rounds up for its own Philox word, in each E2M1 interval: the oracle's
+    # codes are exactly the intended side of each boundary
+    from sr_threshold import threshold_tensor
+    x, want = threshold_tensor(32, 64, seed=0xABCDEF, subseq=4)
+    q = oracle.quantize(x, 6.0, 448.0, oracle.ROW16, oracle.SR, 0xABCDEF, 4).q
+    assert (q.scales == 0xBE).all()
+    codes = np.zeros(x.shape, np.int64)
+    codes[:, 0::2] = q.codes & 0xF
+    codes[:, 1::2] = q.codes >> 4
+    np.testing.assert_array_equal(codes & 7, want)
+    np.testing.assert_array_equal(codes >> 3, np.signbit(x).astype(np.int64))
+    assert 0.3 < np.mean(want[x != 6.0] % 2) < 0.7  # both sides of the boundaries

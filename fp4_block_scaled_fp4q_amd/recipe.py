@@ -112,7 +112,11 @@ class _Fp4LinearFn(torch.autograd.Function):
             aw = st.amax_w.value  # inference: the weight's amax is measured once
         wq, wqt, _ = api.quantize(weight, aw, r.target, api.TILE16x16, api.RNE, transposed=need_grad,
                                   **kw)
-        y = torch.empty((x2.shape[0], weight.shape[0]), dtype=torch.bfloat16, device=x.device)
+        # the output (and, in backward, dX) in the activation's dtype: fp32
+        # activations get fp32 outputs, so their upstream gradients arrive in
+        # fp32 and are quantized without a bf16 rounding first
+        out_dtype = torch.float32 if x.dtype == torch.float32 else torch.bfloat16
+        y = torch.empty((x2.shape[0], weight.shape[0]), dtype=out_dtype, device=x.device)
         api.fp4q_linear_fwd(xq, wq, y)
         if need_grad:
             ctx.module = module
@@ -135,8 +139,10 @@ class _Fp4LinearFn(torch.autograd.Function):
         r = module.recipe
         st = module.state
         dy2 = dy.reshape(-1, dy.shape[-1])
-        if dy2.dtype != torch.bfloat16:
-            dy2 = dy2.to(torch.bfloat16)
+        # bf16 and fp32 gradients are quantized as they come (no extra
+        # rounding step); other dtypes widen exactly to fp32 first
+        if dy2.dtype not in (torch.bfloat16, torch.float32):
+            dy2 = dy2.to(torch.float32)
         if not dy2.is_contiguous():
             dy2 = dy2.contiguous()
         ady = st.amax_dy.update(dy2, ctx.refresh)
@@ -154,7 +160,8 @@ class _Fp4LinearFn(torch.autograd.Function):
             dyqt, _, _ = api.quantize(dy2, ady, t_wg, api.COL16, api.SR, seed, subseq, **kw)
         M, N = dy2.shape
         K = ctx.wqt.rows
-        dx = torch.empty((M, K), dtype=torch.bfloat16, device=dy.device)
+        dx = torch.empty((M, K), dtype=torch.float32 if ctx.x_dtype == torch.float32 else torch.bfloat16,
+                         device=dy.device)
         dw = torch.empty((N, K), dtype=torch.float32, device=dy.device)
         api.fp4q_linear_dgrad(dyq, ctx.wqt, dx)
         api.fp4q_linear_wgrad(dyqt, ctx.xqt, dw)
@@ -169,6 +176,9 @@ class FP4Linear(torch.nn.Module):
 
     weight: [out_features, in_features], float32 or bfloat16 (quantized from
     that dtype; its gradient comes back in it). Inputs are bfloat16 or float32
+    (the output and the input's gradient come in the same dtype: bf16 for
+    bf16 inputs, fp32 for fp32 inputs, whose upstream gradients are then
+    quantized in fp32)
     with in_features a multiple of the block size and of 16; the token count
     must be a multiple of the block size in training (the wgrad operands are
     blocked along tokens).

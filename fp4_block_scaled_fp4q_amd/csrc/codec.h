@@ -149,24 +149,62 @@ __device__ __forceinline__ BlockScale block_scale(uint32_t bamax, float S, doubl
 // the parity tests for fp32 inputs.
 #define FP4Q_ENC2(word, a, b, sel) __builtin_amdgcn_cvt_scalef32_pk_fp4_f32((word), (a), (b), 1.0f, (sel))
 
-// Stochastic rounding of v to an E2M1 code (sign | magnitude) with the
-// 32-bit word w: rounds |v| up to the next magnitude iff w < ceil(p 2^32),
-// p the position of |v| between its two neighbours (w < ceil(x) is w < x for
-// an integer w). In units of 0.5 the grid is 0, 1, 2, 3, 4 then 4, 6, 8 and
-// 8, 12: with A = 2|v|, e = clamp(exponent(A) - 2, 0, 2) and B = A / 2^e,
-// the lower neighbour has code 2e + floor(B) and p = frac(B), both exact in
-// binary32, so p 2^32 is exact before the ceiling. A is clamped to 12, so
-// |v| >= 6 (and Inf) lands exactly on code 7 with p = 0.
-__device__ __forceinline__ uint32_t sr_code(float v, uint32_t w) {
-  const uint32_t u = f2u(v);
-  const float a2 = __builtin_fminf(u2f(u & 0x7FFFFFFFu) * 2.0f, 12.0f);
-  const uint32_t ea = f2u(a2) >> 23;
-  const uint32_t e = min(max(ea, 128u), 130u) - 128u;
-  const float b = __builtin_ldexpf(a2, -(int)e);
-  // fract(B) = B - floor(B) exactly for B >= 0; truncation gives floor(B)
-  const uint32_t t = (uint32_t)__builtin_ceilf(__builtin_amdgcn_fractf(b) * 4294967296.0f);
-  const uint32_t mag = 2u * e + (uint32_t)b + (w < t ? 1u : 0u);
-  return ((u >> 28) & 8u) | mag;
+// Stochastic rounding of v to an E2M1 code (sign | magnitude): |v| rounds up
+// to the next magnitude iff the element's 32-bit word w is below
+// ceil(p 2^32), p the position of |v| between its two neighbours. The word
+// comes in as wz = RZ(w) 2^-32 (sr_unit_words), and the decision is the
+// binary32 comparison wz < p:
+//  * for an integer w and a real P, w < ceil(P) iff w < P;
+//  * for a binary32 value P, w < P iff RZ(w) < P (rounding w toward zero
+//    to 24 significant bits cannot cross a binary32 value from below, and
+//    RZ(w) <= w);
+//  * P = p 2^32 is exact in binary32 here, and both sides scale by 2^-32
+//    exactly.
+// Position: with a = min(|v|, 8) and its exponent clamped to E in {0, 1, 2}
+// (a < 2, a < 4, a <= 8), b = a 2^(1 - E) lies in [0, 4) on a grid of
+// half-units whose spacing is 1: the lower neighbour has code
+// floor(b) + 2 E and p = fract(b), both exact (scaling by a power of two,
+// and fract of a binary32 value). |v| >= 6 (and Inf) ends on code 7.
+__device__ __forceinline__ uint32_t sr_code(float v, float wz) {
+  const float a = __builtin_fminf(__builtin_fabsf(v), 8.0f);
+  const uint32_t e = min(max(f2u(a) >> 23, 127u), 129u);  // biased exponent, clamped
+  const float b = __builtin_ldexpf(a, 128 - (int)e);
+  const float p = __builtin_amdgcn_fractf(b);
+  // 2 (E - 1) ... kept as one value (a shift-add with the offset in a
+  // scalar register) so that the carry-in add of the decision lands on it
+  uint32_t base = 2u * e - 254u;
+  asm("" : "+v"(base));
+  const uint32_t mag = min(base + (uint32_t)b + (wz < p ? 1u : 0u), 7u);
+  return ((f2u(v) >> 28) & 8u) | mag;
+}
+
+// The comparison operands of stochastic rounding for eight Philox words:
+// f[j] = RZ(w[j]) 2^-32. The conversions run with the MODE register's
+// single-precision rounding field set to toward zero, inside one asm block
+// (nothing else can be scheduled into it; the field is restored to nearest
+// even before the block ends, and each MODE write is followed by two wait
+// states before an instruction that depends on it). The scaling by 2^-32
+// is exact in any rounding mode.
+__device__ __forceinline__ void sr_unit_words(const uint32_t* w, float* f) {
+  float t0, t1, t2, t3, t4, t5, t6, t7;
+  asm volatile(
+      "s_setreg_imm32_b32 hwreg(HW_REG_MODE, 0, 2), 3\n\t"
+      "s_nop 1\n\t"
+      "v_cvt_f32_u32 %0, %8\n\t"
+      "v_cvt_f32_u32 %1, %9\n\t"
+      "v_cvt_f32_u32 %2, %10\n\t"
+      "v_cvt_f32_u32 %3, %11\n\t"
+      "v_cvt_f32_u32 %4, %12\n\t"
+      "v_cvt_f32_u32 %5, %13\n\t"
+      "v_cvt_f32_u32 %6, %14\n\t"
+      "v_cvt_f32_u32 %7, %15\n\t"
+      "s_setreg_imm32_b32 hwreg(HW_REG_MODE, 0, 2), 0\n\t"
+      "s_nop 1"
+      : "=&v"(t0), "=&v"(t1), "=&v"(t2), "=&v"(t3), "=&v"(t4), "=&v"(t5), "=&v"(t6), "=&v"(t7)
+      : "v"(w[0]), "v"(w[1]), "v"(w[2]), "v"(w[3]), "v"(w[4]), "v"(w[5]), "v"(w[6]), "v"(w[7]));
+  constexpr float k = 0x1p-32f;
+  f[0] = t0 * k; f[1] = t1 * k; f[2] = t2 * k; f[3] = t3 * k;
+  f[4] = t4 * k; f[5] = t5 * k; f[6] = t6 * k; f[7] = t7 * k;
 }
 
 // Payload code when r overflowed (possible only for a tiny held amax):

@@ -81,18 +81,19 @@ struct Oct<false> {
   }
 };
 
-// Philox words of source elements idx0 .. idx0+7 (idx0 a multiple of 8).
-__device__ __forceinline__ void words8(uint64_t idx0, uint64_t seed, uint32_t subseq, uint32_t* w) {
+// Stochastic-rounding operands of source elements idx0 .. idx0+7 (idx0 a
+// multiple of 8): their Philox words w, as RZ(w) 2^-32 (see sr_code).
+__device__ __forceinline__ void words8(uint64_t idx0, uint64_t seed, uint32_t subseq, float* wz) {
   const U4 r0 = sr_words(idx0 >> 2, subseq, seed);
   const U4 r1 = sr_words((idx0 >> 2) + 1, subseq, seed);
-  w[0] = r0.x; w[1] = r0.y; w[2] = r0.z; w[3] = r0.w;
-  w[4] = r1.x; w[5] = r1.y; w[6] = r1.z; w[7] = r1.w;
+  const uint32_t w[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
+  sr_unit_words(w, wz);
 }
 
 // Codes of the 8 elements of an Oct under one block multiplier (RNE or SR).
 template <bool kBF16, bool kSR>
 __device__ __forceinline__ uint32_t encode_oct(const Oct<kBF16>& x, float mul, bool mul_inf,
-                                               const uint32_t* w) {
+                                               const float* w) {
   uint32_t out = 0u;
   if (__builtin_expect(mul_inf, 0)) {
 #pragma clang loop unroll(full)
@@ -184,7 +185,7 @@ __global__ __launch_bounds__(kRowThreads) void quant_row_kernel(
       m = max(m, o[j].absmax());
     }
     const BlockScale s = block_scale(m, S, S_d, e4m3 != 0);
-    uint32_t w[kBlk];
+    float w[kBlk];
     if (kSR) {
       const uint64_t idx0 = (uint64_t)row * (uint64_t)cols + (uint64_t)blk * kBlk;
 #pragma clang loop unroll(full)
@@ -272,7 +273,7 @@ __global__ __launch_bounds__(kDualThreads<kBlk>()) void quant_dual_kernel(
       if (vr && gc + 8 * j < cols) o[j].load(x + gr * ld_bytes + (gc + 8 * j) * es);
       else o[j].zero();
     }
-    uint32_t w[kBlk];
+    float w[kBlk];
     if (kSR) {
       const uint64_t idx0 = (uint64_t)gr * (uint64_t)cols + (uint64_t)gc;
 #pragma clang loop unroll(full)
@@ -303,9 +304,9 @@ __global__ __launch_bounds__(kDualThreads<kBlk>()) void quant_dual_kernel(
       }
     }
     if (kSR) {
-      uint4* dw = reinterpret_cast<uint4*>(lw + r * kWPitch + 4 * kBlk * q);
+      float4* dw = reinterpret_cast<float4*>(lw + r * kWPitch + 4 * kBlk * q);
 #pragma clang loop unroll(full)
-      for (int k = 0; k < kBlk / 4; ++k) dw[k] = make_uint4(w[4 * k], w[4 * k + 1], w[4 * k + 2], w[4 * k + 3]);
+      for (int k = 0; k < kBlk / 4; ++k) dw[k] = make_float4(w[4 * k], w[4 * k + 1], w[4 * k + 2], w[4 * k + 3]);
     }
   }
   lds_barrier();  // phase 2 reads LDS only; the ROW code stores may still be in flight
@@ -337,7 +338,7 @@ __global__ __launch_bounds__(kDualThreads<kBlk>()) void quant_dual_kernel(
       } else if (kSR) {
 #pragma clang loop unroll(full)
         for (int r = 0; r < kBlk; ++r) {
-          const uint32_t wr = *reinterpret_cast<const uint32_t*>(lw + (kBlk * rb + r) * kWPitch + 4 * c);
+          const float wr = *reinterpret_cast<const float*>(lw + (kBlk * rb + r) * kWPitch + 4 * c);
           cw[r >> 3] |= sr_code(v[r] * s.mul, wr) << (4 * (r & 7));
         }
       } else {
@@ -424,7 +425,7 @@ __global__ __launch_bounds__(kThreads) void quant_tile_kernel(
     const bool mi = __builtin_isinf(b.mul);
 #pragma clang loop unroll(full)
     for (int r = 0; r < 16; ++r) {
-      uint32_t w[8];
+      float w[8];
       if (kSR) words8((uint64_t)(r0 + r) * (uint64_t)cols + (uint64_t)c0, seed, subseq, w);
       const uint32_t word = encode_oct<kBF16, kSR>(v[r], b.mul, mi, w);
       if (valid) *reinterpret_cast<uint32_t*>(codes + code_offset(r0 + r, 4 * oct, rows, cols, k64)) = word;
@@ -501,7 +502,7 @@ __global__ __launch_bounds__(kThreads) void quant_tile32_kernel(
     Oct<kBF16> v;
     if (valid) v.load(x + (r0 + r) * ld_bytes + c0 * es);
     else v.zero();
-    uint32_t w[8];
+    float w[8];
     if (kSR) words8((uint64_t)(r0 + r) * (uint64_t)cols + (uint64_t)c0, seed, subseq, w);
     const uint32_t word = encode_oct<kBF16, kSR>(v, b.mul, mi, w);
     if (valid) *reinterpret_cast<uint32_t*>(codes + code_offset(r0 + r, 4 * oct, rows, cols, k64)) = word;

@@ -48,6 +48,8 @@
 // One kernel serves fwd (A = X, ROW16; B = W, TILE), dgrad (A = dY, ROW16;
 // B = W^T, TILE) and wgrad (A = dY^T, B = X^T, both quantized along tokens):
 // both operands are stored contiguous along the contraction.
+#include <atomic>
+
 #include "codec.h"
 #include "kernels.h"
 
@@ -85,7 +87,10 @@ constexpr int kPM = 128;  // tile of the probe-mode kernel
 constexpr int kModeRound32 = (1 << 11) | 1;
 constexpr int kThreads = 256;
 constexpr int kChunks = BK / 8;              // 16-byte chunks per LDS row
-constexpr int kGroupM = 8;                   // M-tiles per scheduling group
+#ifndef FP4Q_GEMM_GROUP_M
+#define FP4Q_GEMM_GROUP_M 8
+#endif
+constexpr int kGroupM = FP4Q_GEMM_GROUP_M;   // M-tiles per scheduling group
 
 // Codes and scales of one 64-element row segment (4 blocks of 16, or 2 of
 // 32). The scale bytes are kept as loaded (s0: the first two, s1: the next
@@ -122,7 +127,7 @@ __device__ __forceinline__ uint32_t seg_scale(const RowSeg& g, int j, bool blk32
 // 16-bit scale load repeats the first for blocks of 32, so it stays inside
 // the row. kK64: the K64 packing, where a segment is the row's 32 bytes of
 // k tile k0 / 64 and the workgroup's consecutive rows are adjacent.
-template <bool kFmt, bool kK64>
+template <bool kFmt, bool kK64, bool kNT = false>
 __device__ __forceinline__ RowSeg load_seg_full(const uint8_t* __restrict__ codes,
                                                 const uint8_t* __restrict__ scales, int64_t rows,
                                                 int64_t K, int tile_shift, bool blk32, int64_t r,
@@ -132,12 +137,18 @@ __device__ __forceinline__ RowSeg load_seg_full(const uint8_t* __restrict__ code
   const int64_t srows = rows >> tile_shift;
   const uint8_t* cp = kK64 ? codes + kt * (rows * 32) + r * 32 : codes + r * (K / 2) + k0 / 2;
   RowSeg g;
-  g.c0 = *reinterpret_cast<const uint4*>(cp);
-  g.c1 = *reinterpret_cast<const uint4*>(cp + 16);
+  if constexpr (kNT) {
+    g.c0 = load_nt16(cp);
+    g.c1 = load_nt16(cp + 16);
+  } else {
+    g.c0 = *reinterpret_cast<const uint4*>(cp);
+    g.c1 = *reinterpret_cast<const uint4*>(cp + 16);
+  }
   if (!kFmt) {
-    g.s0 = *reinterpret_cast<const uint32_t*>(
+    const uint32_t* sp = reinterpret_cast<const uint32_t*>(
         kK64 ? scales + kt * (srows * 4) + (r >> tile_shift) * 4
              : scales + (r >> tile_shift) * (K / 16) + k0 / 16);
+    g.s0 = kNT ? __builtin_nontemporal_load(sp) : *sp;
     g.s1 = 0u;
     return g;
   }
@@ -189,15 +200,21 @@ __device__ __forceinline__ RowSeg load_seg_tail(const uint8_t* __restrict__ code
   return g;
 }
 
-template <bool kFullK, bool kFmt, bool kK64>
+template <bool kFullK, bool kFmt, bool kK64, bool kNT = false>
 __device__ __forceinline__ RowSeg load_seg(const uint8_t* __restrict__ codes,
                                            const uint8_t* __restrict__ scales, int64_t rows,
                                            int64_t K, int tile_shift, bool blk32, int64_t r,
                                            int64_t k0) {
   static_assert(kFullK || !kK64, "the K64 packing needs K % 64 == 0");
-  return kFullK ? load_seg_full<kFmt, kK64>(codes, scales, rows, K, tile_shift, blk32, r, k0)
+  return kFullK ? load_seg_full<kFmt, kK64, kNT>(codes, scales, rows, K, tile_shift, blk32, r, k0)
                 : load_seg_tail<kFmt>(codes, scales, rows, K, tile_shift, blk32, r, k0);
 }
+
+// Nontemporal loads for the B operand (the operand a tile group streams
+// through while its A panel stays in the L2).
+#ifndef FP4Q_GEMM_NT_B
+#define FP4Q_GEMM_NT_B 0
+#endif
 
 // 8 codes (one 32-bit word, element e in bits 4e+3:4e) of a block with
 // decoded scale dec -> 8 bf16, element order kept.
@@ -351,8 +368,8 @@ __device__ __forceinline__ void gemm_tile(
       const int q = tid + i * kT;
       g[i] = q < kBM
                  ? load_seg<kFullK, kFmt, kK64>(a_codes, a_scales, M, K, a_shift, a_blk32, m0 + q, k0)
-                 : load_seg<kFullK, kFmt, kK64>(b_codes, b_scales, N, K, b_shift, b_blk32, n0 + (q - kBM),
-                                                k0);
+                 : load_seg<kFullK, kFmt, kK64, (bool)FP4Q_GEMM_NT_B && !kProbe>(
+                       b_codes, b_scales, N, K, b_shift, b_blk32, n0 + (q - kBM), k0);
     }
   };
   // one decode8 piece p (0 .. kPieces-1) of block s into buffer `buf`
@@ -630,7 +647,9 @@ __global__ __launch_bounds__(64 * kWavesM * kWavesN) void gemm_kernel(
     void* __restrict__ y, int nwg) {
   if constexpr (kFmt || kProbe) {
     // one tile per workgroup (the format-generic kernel would pass 256
-    // VGPRs inside a tile loop)
+    // VGPRs inside a tile loop); the grid is rounded up to a multiple of 8,
+    // so workgroups past the last logical one have no tile
+    if ((int)blockIdx.x >= nwg) return;
     gemm_tile<kBM, kBN, kFullK, kF32Out, kWavesM, kWavesN, kSwz, kProbe, kFmt, kK64, false>(
         a_codes, a_scales, a_shift, a_S, b_codes, b_scales, b_shift, b_S, M, N, K, tiles_m, tiles_n,
         snap_log2, fmt, split_local, y, (int)blockIdx.x, (int)threadIdx.x, nullptr);
@@ -684,14 +703,48 @@ __global__ __launch_bounds__(256) void zero_split_tiles(float* __restrict__ y, i
 
 namespace {
 
-// Workgroups of the default kernel that run at once on the current device:
-// one per compute unit (its LDS use allows one per CU).
-int concurrent_workgroups() {
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-    return 256;
+// Per-device facts the launcher needs, looked up once per device and kept
+// in lock-free caches (a race only repeats an idempotent lookup).
+constexpr int kMaxDevices = 64;
+
+// Workgroups of the default kernel that run at once on device dev: one per
+// compute unit (its LDS use allows one per CU).
+int concurrent_workgroups(int dev) {
+  static std::atomic<int> cache[kMaxDevices];
+  if (dev < 0 || dev >= kMaxDevices) dev = 0;
+  int cus = cache[dev].load(std::memory_order_relaxed);
+  if (cus > 0) return cus;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    cus = 256;
+  cache[dev].store(cus, std::memory_order_relaxed);
   return cus;
+}
+
+// The dynamic LDS limit of kernel fn on device dev, raised once per
+// (kernel, device): one bit per device in a mask kept per kernel.
+hipError_t allow_lds(const void* fn, int dev, int bytes) {
+  struct Entry {
+    std::atomic<const void*> fn;
+    std::atomic<uint64_t> devs;
+  };
+  static Entry table[64];
+  const uint64_t bit = (dev >= 0 && dev < kMaxDevices) ? (uint64_t(1) << dev) : 0;
+  Entry* e = nullptr;
+  for (Entry& t : table) {
+    const void* cur = t.fn.load(std::memory_order_acquire);
+    if (cur == fn) { e = &t; break; }
+    if (cur == nullptr) {
+      const void* expected = nullptr;
+      if (t.fn.compare_exchange_strong(expected, fn, std::memory_order_acq_rel) || expected == fn) {
+        e = &t;
+        break;
+      }
+    }
+  }
+  if (e && bit && (e->devs.load(std::memory_order_acquire) & bit)) return hipSuccess;
+  const hipError_t err = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (err == hipSuccess && e && bit) e->devs.fetch_or(bit, std::memory_order_acq_rel);
+  return err;
 }
 
 template <int kBM, int kBN, int kWM, int kWN, int kSW, bool kProbe, bool kFmt>
@@ -714,7 +767,10 @@ hipError_t launch_kernel(const QOperand& a, const QOperand& b, void* y, int y_es
   else
     fn = y_es == 4 ? (const void*)gemm_kernel<kBM, kBN, false, true, kWM, kWN, kSW, kProbe, kFmt, false>
                    : (const void*)gemm_kernel<kBM, kBN, false, false, kWM, kWN, kSW, kProbe, kFmt, false>;
-  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  e = allow_lds(fn, dev, (int)lds_bytes);
   if (e != hipSuccess) return e;
   // split tail: when the tiles fill the last round of workgroups at most
   // half way, run each of those tiles as two K halves (fp32 output only)
@@ -722,7 +778,7 @@ hipError_t launch_kernel(const QOperand& a, const QOperand& b, void* y, int y_es
   const int nk = (int)((K + BK - 1) / BK);
   const int per_xcd = (ntiles + 7) / 8;
   int split_local = -1;
-  const int cwg = (!kProbe && y_es == 4) ? concurrent_workgroups() : 1;  // one per CU
+  const int cwg = (!kProbe && y_es == 4) ? concurrent_workgroups(dev) : 1;  // one per CU
   const int rem = ntiles % cwg;
 #ifndef FP4Q_NO_SPLIT_TAIL
   if (!kProbe && y_es == 4 && ntiles % 8 == 0 && rem > 0 && rem % 8 == 0 && 2 * rem <= cwg && nk >= 2 &&
@@ -740,7 +796,7 @@ hipError_t launch_kernel(const QOperand& a, const QOperand& b, void* y, int y_es
   // workgroup of this kernel per CU at a time)
   int rep = 1;
   if (!kProbe && !kFmt) {
-    const int64_t cw = concurrent_workgroups();
+    const int64_t cw = concurrent_workgroups(dev);
     const int64_t rounds1 = (nwg + cw - 1) / cw;
     const int64_t phys2 = 8 * (((nwg + 7) / 8 + 1) / 2);
     if (2 * ((phys2 + cw - 1) / cw) <= rounds1) rep = 2;

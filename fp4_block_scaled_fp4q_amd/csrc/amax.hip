@@ -31,6 +31,24 @@ __device__ __forceinline__ uint32_t fold(uint32_t acc, const uint4 v) {
   return max(acc, max(max(w0, w1), max(w2, w3)));
 }
 
+// Maximum over the 64 lanes of a wave, valid in lane 0: DPP steps inside
+// each row of 16 lanes (swap neighbours, swap pairs, mirror each half row,
+// mirror the row), a ds_swizzle exchange between the two rows of each
+// 32-lane half (xor 16), then the two halves' lanes 0 and 32.
+template <int kCtrl>
+__device__ __forceinline__ uint32_t dpp(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kCtrl, 0xF, 0xF, false);
+}
+
+__device__ __forceinline__ uint32_t wave_max_lane0(uint32_t m) {
+  m = max(m, dpp<0xB1>(m));   // quad_perm [1, 0, 3, 2]
+  m = max(m, dpp<0x4E>(m));   // quad_perm [2, 3, 0, 1]
+  m = max(m, dpp<0x141>(m));  // row_half_mirror
+  m = max(m, dpp<0x140>(m));  // row_mirror
+  m = max(m, (uint32_t)__builtin_amdgcn_ds_swizzle((int)m, 0x401F));  // and 0x1F, xor 0x10
+  return max((uint32_t)__builtin_amdgcn_readlane((int)m, 0), (uint32_t)__builtin_amdgcn_readlane((int)m, 32));
+}
+
 // Workgroup-wide maximum, then at most one atomic per workgroup, skipped
 // when the output already holds a value at least as large (atomics on one
 // address serialize, so their number is kept to a few hundred).
@@ -38,8 +56,7 @@ template <bool kBF16>
 __device__ __forceinline__ void finish(uint32_t acc, uint32_t* out) {
   __shared__ uint32_t wmax[4];
   uint32_t m = kBF16 ? (max(acc & 0xFFFFu, acc >> 16) << 16) : acc;
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
+  m = wave_max_lane0(m);
   if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
   __syncthreads();
   if (threadIdx.x == 0) {

@@ -325,19 +325,8 @@ def main():
 
     # traffic from committed rocprofv3 counters, valid only for this GEMM
     # source built with these flags
-    traffic = None
-    tf = os.path.join(ROOT, "profiles", "gemm_ffn_up_traffic.json")
-    if os.path.exists(tf):
-        try:
-            rec = json.load(open(tf))
-            pkg = os.path.join(ROOT, "fp4_block_scaled_fp4q_amd")
-            src = open(os.path.join(pkg, "csrc", "gemm.hip"), "rb").read()
-            flags = open(os.path.join(pkg, "build.py"), "rb").read()
-            if (rec.get("gemm_hip_sha256") == hashlib.sha256(src).hexdigest()
-                    and rec.get("build_py_sha256") == hashlib.sha256(flags).hexdigest()):
-                traffic = rec.get("bytes_per_launch")
-        except Exception:
-            traffic = None
+    rec = _record("gemm_ffn_up_traffic.json", {"gemm_hip_sha256": "csrc/gemm.hip"})
+    traffic = rec.get("bytes_per_launch") if rec else None
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -390,23 +379,22 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def _record(name: str, src: str):
-    """A committed rocprofv3 record under profiles/, used only while the
-    kernel source it was taken from (and the build flags) are unchanged."""
+def _record(name: str, files: dict):
+    """A committed rocprofv3 record under profiles/, used only while every
+    source it was taken from (and the build flags) is unchanged: files maps
+    the record's *_sha256 keys to paths under the package."""
     path = os.path.join(ROOT, "profiles", name)
     if not os.path.exists(path):
         return None
     try:
         rec = json.load(open(path))
         pkg = os.path.join(ROOT, "fp4_block_scaled_fp4q_amd")
-        code = open(os.path.join(pkg, "csrc", src), "rb").read()
-        flags = open(os.path.join(pkg, "build.py"), "rb").read()
-        if (rec.get("source_sha256") == hashlib.sha256(code).hexdigest()
-                and rec.get("build_py_sha256") == hashlib.sha256(flags).hexdigest()):
-            return rec
+        for key, rel in dict(files, build_py_sha256="build.py").items():
+            if rec.get(key) != hashlib.sha256(open(os.path.join(pkg, rel), "rb").read()).hexdigest():
+                return None
+        return rec
     except Exception:
         return None
-    return None
 
 
 def valu_line(us: float, launch: str):
@@ -414,7 +402,7 @@ def valu_line(us: float, launch: str):
     VALU instructions per launch (rocprofv3 SQ_INSTS_VALU, committed in
     profiles/codec_valu_counts.json for the current quantize source) over
     its measured duration, against VALU_PEAK_WAVE_INSTR."""
-    rec = _record("codec_valu_counts.json", "quantize.hip")
+    rec = _record("codec_valu_counts.json", {"source_sha256": "csrc/quantize.hip", "codec_h_sha256": "csrc/codec.h"})
     if rec is None or launch not in rec.get("per_launch", {}):
         return None
     n = rec["per_launch"][launch]["sq_insts_valu"]

@@ -82,9 +82,6 @@ constexpr int BM = 256;   // tile of the default kernel
 constexpr int BN = 256;
 constexpr int BK = 64;    // k tile (also the slice of the probe mode)
 constexpr int kPM = 128;  // tile of the probe-mode kernel
-// s_setreg operand for MODE bits 1:0, the single-precision rounding mode
-// (0: nearest even, 3: toward zero): size 2, offset 0, register MODE (1)
-constexpr int kModeRound32 = (1 << 11) | 1;
 constexpr int kThreads = 256;
 constexpr int kChunks = BK / 8;              // 16-byte chunks per LDS row
 #ifndef FP4Q_GEMM_GROUP_M
@@ -522,18 +519,28 @@ __device__ __forceinline__ void gemm_tile(
       // add the slice partials to the running sums with round-toward-zero.
       // The MODE rounding field governs these VALU additions only: MFMA
       // results are the same under either mode (checked on 65536 random
-      // outputs), so MFMAs still in flight need no draining first.
+      // outputs). The compiler does not model the additions' dependence on
+      // MODE (a plain fp32 add may legally move across a MODE write, and
+      // one k tile's additions of each unrolled pair did), so the two MODE
+      // writes and every addition are volatile asm statements, which keep
+      // their order: all 64 additions run inside the window. The asm hides
+      // the additions' reads of the matrix core's results from the
+      // compiler's hazard tracking, so the window opens with 24 wait states
+      // (more than a 16-pass MFMA result needs before a VALU read, and the
+      // MODE write's own two).
       __builtin_amdgcn_sched_barrier(0);
-      __builtin_amdgcn_s_setreg(kModeRound32, 3);
-      __builtin_amdgcn_sched_barrier(0);
+      asm volatile("s_setreg_imm32_b32 hwreg(HW_REG_MODE, 0, 2), 3\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 #pragma unroll
       for (int i = 0; i < kFM; ++i)
 #pragma unroll
         for (int j = 0; j < kFN; ++j)
 #pragma unroll
-          for (int e = 0; e < 16; ++e) tot[i][j][e] = tot[i][j][e] + acc[i][j][e];
-      __builtin_amdgcn_sched_barrier(0);
-      __builtin_amdgcn_s_setreg(kModeRound32, 0);
+          for (int e = 0; e < 16; ++e) {
+            float t;
+            asm volatile("v_add_f32 %0, %1, %2" : "=v"(t) : "v"(tot[i][j][e]), "v"(acc[i][j][e]));
+            tot[i][j][e] = t;
+          }
+      asm volatile("s_setreg_imm32_b32 hwreg(HW_REG_MODE, 0, 2), 0\n\ts_nop 1" ::: "memory");
       __builtin_amdgcn_sched_barrier(0);
     }
     if (!FP4Q_GEMM_ROTATE) lds_barrier();

@@ -325,7 +325,7 @@ def main():
 
     # traffic from committed rocprofv3 counters, valid only for this GEMM
     # source built with these flags
-    rec = _record("gemm_ffn_up_traffic.json", {"gemm_hip_sha256": "csrc/gemm.hip"})
+    rec = _record("gemm_ffn_up_traffic.json", {"gemm_hip_sha256": "csrc/gemm.hip", "codec_h_sha256": "csrc/codec.h"})
     traffic = rec.get("bytes_per_launch") if rec else None
 
     cpu = None

@@ -149,42 +149,39 @@ __device__ __forceinline__ BlockScale block_scale(uint32_t bamax, float S, doubl
 // the parity tests for fp32 inputs.
 #define FP4Q_ENC2(word, a, b, sel) __builtin_amdgcn_cvt_scalef32_pk_fp4_f32((word), (a), (b), 1.0f, (sel))
 
-// Stochastic rounding of v to an E2M1 code (sign | magnitude): |v| rounds up
-// to the next magnitude iff the element's 32-bit word w is below
-// ceil(p 2^32), p the position of |v| between its two neighbours. The word
-// comes in as wz = RZ(w) 2^-32 (sr_unit_words), and the decision is the
-// binary32 comparison wz < p:
-//  * for an integer w and a real P, w < ceil(P) iff w < P;
-//  * for a binary32 value P, w < P iff RZ(w) < P (rounding w toward zero
-//    to 24 significant bits cannot cross a binary32 value from below, and
-//    RZ(w) <= w);
-//  * P = p 2^32 is exact in binary32 here, and both sides scale by 2^-32
-//    exactly.
-// Position: with a = min(|v|, 8) and its exponent clamped to E in {0, 1, 2}
-// (a < 2, a < 4, a <= 8), b = a 2^(1 - E) lies in [0, 4) on a grid of
-// half-units whose spacing is 1: the lower neighbour has code
-// floor(b) + 2 E and p = fract(b), both exact (scaling by a power of two,
-// and fract of a binary32 value). |v| >= 6 (and Inf) ends on code 7.
-__device__ __forceinline__ uint32_t sr_code(float v, float wz) {
-  const float a = __builtin_fminf(__builtin_fabsf(v), 8.0f);
-  const uint32_t e = min(max(f2u(a) >> 23, 127u), 129u);  // biased exponent, clamped
-  const float b = __builtin_ldexpf(a, 128 - (int)e);
-  const float p = __builtin_amdgcn_fractf(b);
-  // 2 (E - 1) ... kept as one value (a shift-add with the offset in a
-  // scalar register) so that the carry-in add of the decision lands on it
-  uint32_t base = 2u * e - 254u;
-  asm("" : "+v"(base));
-  const uint32_t mag = min(base + (uint32_t)b + (wz < p ? 1u : 0u), 7u);
-  return ((f2u(v) >> 28) & 8u) | mag;
-}
+// Stochastic rounding to E2M1 (sign | magnitude): |v| rounds up to the
+// next magnitude iff the element's 32-bit word w is below ceil(p 2^32), p
+// the position of |v| between its neighbours lo <= |v| < hi (spacing
+// s = hi - lo, 1/2 below 2, 1 below 4, 2 above). The decision is made
+// exactly in binary32 and the code is produced by a hardware conversion:
+//  1. w < ceil(P) iff w < P for integer w and real P = p 2^32; P is a
+//     binary32 value (p = (|v| - lo) / s is), so w < P iff RZ(w) < P, i.e.
+//     q < p / 2 with q = RZ(w) 2^-33 (exact scaling; p / 2 is exact too).
+//  2. q < p / 2 iff q' <= p / 2, where q' is the binary32 successor of q
+//     (bit pattern plus one; no binary32 value lies strictly between), i.e.
+//     iff A = |v| - q' s2 >= lo, with s2 = 2 s (the binade base of |v|,
+//     at least 1) and q' <= 1/2, so q' s2 <= s.
+//  3. z = RZ(RZ(A) + s) lies in [hi, hi + s) when A >= lo and in [lo, hi)
+//     otherwise (lo, hi and lo - s are binary32 values, the rounding is
+//     toward zero, and the spacing above hi is at least s), so rounding z
+//     toward zero onto the E2M1 grid gives hi or lo as required. |v| >= 6
+//     (lo = 6) gives z >= 6, which the conversion saturates to 6.
+//  4. Toward zero onto the grid is the gfx950 stochastic conversion
+//     v_cvt_scalef32_sr_pk_fp4_f32 with random operand 0 (it adds the
+//     random bits below the kept ones before truncating), checked against
+//     floor-to-grid on every binade down to the subnormals; it keeps the
+//     sign, which z gets from v (rounding toward zero is symmetric).
+// Per element: one max and one mask for s2, two fused multiply-adds under
+// the MODE register's toward-zero rounding, one bit insert for the sign
+// and half a conversion.
 
-// The comparison operands of stochastic rounding for eight Philox words:
-// f[j] = RZ(w[j]) 2^-32. The conversions run with the MODE register's
-// single-precision rounding field set to toward zero, inside one asm block
-// (nothing else can be scheduled into it; the field is restored to nearest
-// even before the block ends, and each MODE write is followed by two wait
-// states before an instruction that depends on it). The scaling by 2^-32
-// is exact in any rounding mode.
+// q' of step 2 for eight Philox words: f[j] = succ(RZ(w[j]) 2^-33). The
+// conversions run with the MODE register's single-precision rounding field
+// set to toward zero, inside one asm block (nothing else can be scheduled
+// into it; the field is restored to nearest even before the block ends,
+// and each MODE write is followed by two wait states before an instruction
+// that depends on it). The scaling by 2^-33 is exact in any rounding mode;
+// for w = 0 the successor is the smallest subnormal.
 __device__ __forceinline__ void sr_unit_words(const uint32_t* w, float* f) {
   float t0, t1, t2, t3, t4, t5, t6, t7;
   asm volatile(
@@ -202,9 +199,62 @@ __device__ __forceinline__ void sr_unit_words(const uint32_t* w, float* f) {
       "s_nop 1"
       : "=&v"(t0), "=&v"(t1), "=&v"(t2), "=&v"(t3), "=&v"(t4), "=&v"(t5), "=&v"(t6), "=&v"(t7)
       : "v"(w[0]), "v"(w[1]), "v"(w[2]), "v"(w[3]), "v"(w[4]), "v"(w[5]), "v"(w[6]), "v"(w[7]));
-  constexpr float k = 0x1p-32f;
-  f[0] = t0 * k; f[1] = t1 * k; f[2] = t2 * k; f[3] = t3 * k;
-  f[4] = t4 * k; f[5] = t5 * k; f[6] = t6 * k; f[7] = t7 * k;
+  constexpr float k = 0x1p-33f;
+  f[0] = u2f(f2u(t0 * k) + 1u); f[1] = u2f(f2u(t1 * k) + 1u);
+  f[2] = u2f(f2u(t2 * k) + 1u); f[3] = u2f(f2u(t3 * k) + 1u);
+  f[4] = u2f(f2u(t4 * k) + 1u); f[5] = u2f(f2u(t5 * k) + 1u);
+  f[6] = u2f(f2u(t6 * k) + 1u); f[7] = u2f(f2u(t7 * k) + 1u);
+}
+
+// z of step 3 for four elements: z = RZ(RZ(|v| - q s2) + s2 / 2), both
+// fused multiply-adds under toward-zero rounding in one asm block (MODE
+// handling as in sr_unit_words).
+__device__ __forceinline__ void sr_z4(const float* v, const float* q, const float* s2, float* z) {
+  float z0, z1, z2, z3;
+  asm volatile(
+      "s_setreg_imm32_b32 hwreg(HW_REG_MODE, 0, 2), 3\n\t"
+      "s_nop 1\n\t"
+      "v_fma_f32 %0, -%4, %8, |%12|\n\t"
+      "v_fma_f32 %1, -%5, %9, |%13|\n\t"
+      "v_fma_f32 %2, -%6, %10, |%14|\n\t"
+      "v_fma_f32 %3, -%7, %11, |%15|\n\t"
+      "v_fma_f32 %0, %8, 0.5, %0\n\t"
+      "v_fma_f32 %1, %9, 0.5, %1\n\t"
+      "v_fma_f32 %2, %10, 0.5, %2\n\t"
+      "v_fma_f32 %3, %11, 0.5, %3\n\t"
+      "s_setreg_imm32_b32 hwreg(HW_REG_MODE, 0, 2), 0\n\t"
+      "s_nop 1"
+      : "=&v"(z0), "=&v"(z1), "=&v"(z2), "=&v"(z3)
+      : "v"(q[0]), "v"(q[1]), "v"(q[2]), "v"(q[3]), "v"(s2[0]), "v"(s2[1]), "v"(s2[2]), "v"(s2[3]),
+        "v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3]));
+  z[0] = z0; z[1] = z1; z[2] = z2; z[3] = z3;
+}
+
+// Stochastic-rounding codes of v[0..7] (packed, even element in the low
+// nibble), q[j] from sr_unit_words. The conversion writes one byte of its
+// destination and keeps the other three; it is written as asm with the
+// destination read and written, since the compiler's builtin for it does
+// not carry the kept bytes through.
+__device__ __forceinline__ uint32_t sr8(const float* v, const float* q) {
+  float s2[8], z[8];
+#pragma clang loop unroll(full)
+  for (int j = 0; j < 8; ++j) s2[j] = u2f(max(f2u(v[j]) & 0x7F800000u, 0x3F800000u));
+  sr_z4(v, q, s2, z);
+  sr_z4(v + 4, q + 4, s2 + 4, z + 4);
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  double zp[4];
+#pragma clang loop unroll(full)
+  for (int k = 0; k < 4; ++k)
+    zp[k] = __builtin_bit_cast(double, f32x2_t{u2f((f2u(v[2 * k]) & 0x80000000u) | f2u(z[2 * k])),
+                                               u2f((f2u(v[2 * k + 1]) & 0x80000000u) | f2u(z[2 * k + 1]))});
+  uint32_t out = 0u;
+  asm("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, 0, 1.0\n\t"
+      "v_cvt_scalef32_sr_pk_fp4_f32 %0, %2, 0, 1.0 op_sel:[0,0,1,0]\n\t"
+      "v_cvt_scalef32_sr_pk_fp4_f32 %0, %3, 0, 1.0 op_sel:[0,0,0,1]\n\t"
+      "v_cvt_scalef32_sr_pk_fp4_f32 %0, %4, 0, 1.0 op_sel:[0,0,1,1]"
+      : "+v"(out)
+      : "v"(zp[0]), "v"(zp[1]), "v"(zp[2]), "v"(zp[3]));
+  return out;
 }
 
 // Payload code when r overflowed (possible only for a tiny held amax):

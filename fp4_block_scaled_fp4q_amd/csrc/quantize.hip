@@ -82,7 +82,7 @@ struct Oct<false> {
 };
 
 // Stochastic-rounding operands of source elements idx0 .. idx0+7 (idx0 a
-// multiple of 8): their Philox words w, as RZ(w) 2^-32 (see sr_code).
+// multiple of 8): their Philox words w, as succ(RZ(w) 2^-33) (see sr8).
 __device__ __forceinline__ void words8(uint64_t idx0, uint64_t seed, uint32_t subseq, float* wz) {
   const U4 r0 = sr_words(idx0 >> 2, subseq, seed);
   const U4 r1 = sr_words((idx0 >> 2) + 1, subseq, seed);
@@ -101,8 +101,10 @@ __device__ __forceinline__ uint32_t encode_oct(const Oct<kBF16>& x, float mul, b
     return out;
   }
   if (kSR) {
+    float v[8];
 #pragma clang loop unroll(full)
-    for (int j = 0; j < 8; ++j) out |= sr_code(x.get(j) * mul, w[j]) << (4 * j);
+    for (int j = 0; j < 8; ++j) v[j] = x.get(j) * mul;
+    out = sr8(v, w);
   } else {
     out = FP4Q_ENC2(out, x.get(0) * mul, x.get(1) * mul, 0);
     out = FP4Q_ENC2(out, x.get(2) * mul, x.get(3) * mul, 1);
@@ -337,9 +339,14 @@ __global__ __launch_bounds__(kDualThreads<kBlk>()) void quant_dual_kernel(
         for (int r = 0; r < kBlk; ++r) cw[r >> 3] |= inf_code(v[r]) << (4 * (r & 7));
       } else if (kSR) {
 #pragma clang loop unroll(full)
-        for (int r = 0; r < kBlk; ++r) {
-          const float wr = *reinterpret_cast<const float*>(lw + (kBlk * rb + r) * kWPitch + 4 * c);
-          cw[r >> 3] |= sr_code(v[r] * s.mul, wr) << (4 * (r & 7));
+        for (int j = 0; j < kOcts; ++j) {
+          float vs[8], wr[8];
+#pragma clang loop unroll(full)
+          for (int i = 0; i < 8; ++i) {
+            vs[i] = v[8 * j + i] * s.mul;
+            wr[i] = *reinterpret_cast<const float*>(lw + (kBlk * rb + 8 * j + i) * kWPitch + 4 * c);
+          }
+          cw[j] = sr8(vs, wr);
         }
       } else {
 #pragma clang loop unroll(full)

@@ -165,13 +165,16 @@ __device__ __forceinline__ BlockScale block_scale(uint32_t bamax, float S, doubl
 //     otherwise (lo, hi and lo - s are binary32 values, the rounding is
 //     toward zero, and the spacing above hi is at least s), so rounding z
 //     toward zero onto the E2M1 grid gives hi or lo as required. |v| >= 6
-//     (lo = 6) gives z >= 6, which the conversion saturates to 6.
+//     (lo = 6) gives z >= 6, which the conversion saturates to 6; s2 is
+//     clamped to [1, 4] (its value for |v| in [4, 8)), so that |v| = Inf (a
+//     finite x times a finite multiplier can overflow) gives z = Inf, not
+//     Inf - Inf.
 //  4. Toward zero onto the grid is the gfx950 stochastic conversion
 //     v_cvt_scalef32_sr_pk_fp4_f32 with random operand 0 (it adds the
 //     random bits below the kept ones before truncating), checked against
 //     floor-to-grid on every binade down to the subnormals; it keeps the
 //     sign, which z gets from v (rounding toward zero is symmetric).
-// Per element: one max and one mask for s2, two fused multiply-adds under
+// Per element: one median and one mask for s2, two fused multiply-adds under
 // the MODE register's toward-zero rounding, one bit insert for the sign
 // and half a conversion.
 
@@ -238,7 +241,7 @@ __device__ __forceinline__ void sr_z4(const float* v, const float* q, const floa
 __device__ __forceinline__ uint32_t sr8(const float* v, const float* q) {
   float s2[8], z[8];
 #pragma clang loop unroll(full)
-  for (int j = 0; j < 8; ++j) s2[j] = u2f(max(f2u(v[j]) & 0x7F800000u, 0x3F800000u));
+  for (int j = 0; j < 8; ++j) s2[j] = u2f(min(max(f2u(v[j]) & 0x7F800000u, 0x3F800000u), 0x40800000u));
   sr_z4(v, q, s2, z);
   sr_z4(v + 4, q + 4, s2 + 4, z + 4);
   typedef float f32x2_t __attribute__((ext_vector_type(2)));

@@ -113,11 +113,14 @@ def test_exhaustive_bf16_payloads(rnd):
     assert_quant_equal(g, o, "payload sweep")
 
 
+@pytest.mark.parametrize("rnd", [0, 1])
 @pytest.mark.parametrize("held,T", [(1.0, 448.0), (1e-3, 448.0), (3e4, 2048.0), (2.5e-30, 448.0)])
-def test_exhaustive_block_scales(held, T):
+def test_exhaustive_block_scales(held, T, rnd):
     # one block per positive finite bf16 bamax: exercises both per-block
     # divisions, the UE5M3 rounding (incl. ties), zero/saturation repair and
-    # the overflowing-multiplier path
+    # the overflowing-multiplier path; with held = 2.5e-30 the saturated
+    # scales let x * r overflow to +-Inf for the largest inputs, which both
+    # roundings must encode as +-6
     v = _all_bf16(0.0, 3.4e38)
     v = v[(v & 0x8000) == 0]
     v = v[v != 0]
@@ -127,8 +130,8 @@ def test_exhaustive_block_scales(held, T):
     bits[:, 2] = (v.astype(np.uint32) - 1).clip(0).astype(np.uint16)  # just below bamax
     bits[:, 3] = (v >> 1)                                               # about sqrt-ish smaller
     x = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16)
-    g, o = quant_both(x, held, "row16", 0, T)
-    assert_quant_equal(g, o, f"held={held} T={T}")
+    g, o = quant_both(x, held, "row16", rnd, T, seed=11)
+    assert_quant_equal(g, o, f"held={held} T={T} rnd={rnd}")
 
 
 @pytest.mark.parametrize("held", [0.0, float("inf"), float("nan"), 1e-40, 1e-36])

@@ -237,7 +237,10 @@ __device__ __forceinline__ void sr_z4(const float* v, const float* q, const floa
 // nibble), q[j] from sr_unit_words. The conversion writes one byte of its
 // destination and keeps the other three; it is written as asm with the
 // destination read and written, since the compiler's builtin for it does
-// not carry the kept bytes through.
+// not carry the kept bytes through. A scaled conversion that writes a
+// byte other than the lowest is followed by one wait state before an
+// instruction that reads its result, as the compiler schedules the
+// round-to-nearest form of the same chain.
 __device__ __forceinline__ uint32_t sr8(const float* v, const float* q) {
   float s2[8], z[8];
 #pragma clang loop unroll(full)
@@ -253,8 +256,11 @@ __device__ __forceinline__ uint32_t sr8(const float* v, const float* q) {
   uint32_t out = 0u;
   asm("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, 0, 1.0\n\t"
       "v_cvt_scalef32_sr_pk_fp4_f32 %0, %2, 0, 1.0 op_sel:[0,0,1,0]\n\t"
+      "s_nop 0\n\t"
       "v_cvt_scalef32_sr_pk_fp4_f32 %0, %3, 0, 1.0 op_sel:[0,0,0,1]\n\t"
-      "v_cvt_scalef32_sr_pk_fp4_f32 %0, %4, 0, 1.0 op_sel:[0,0,1,1]"
+      "s_nop 0\n\t"
+      "v_cvt_scalef32_sr_pk_fp4_f32 %0, %4, 0, 1.0 op_sel:[0,0,1,1]\n\t"
+      "s_nop 0"
       : "+v"(out)
       : "v"(zp[0]), "v"(zp[1]), "v"(zp[2]), "v"(zp[3]));
   return out;

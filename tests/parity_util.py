@@ -194,3 +194,33 @@ def check_gemm_elementwise(got: torch.Tensor, ref: np.ndarray, bound: np.ndarray
     fro = rel_fro(g, round_out(ref, got.dtype))
     assert fro <= GEMM_TOL, f"{what}: rel Frobenius {fro:.3e}"
     return fro
+
+
+def lsb_exp(x: np.ndarray) -> np.ndarray:
+    """Exponent of the lowest set bit of each nonzero (binary-fraction)
+    float64 value; a large number (2^20) for zeros."""
+    ax = np.abs(x)
+    nz = ax > 0
+    m, e = np.frexp(np.where(nz, ax, 1.0))
+    v = (m * 2.0 ** 53).astype(np.int64)
+    tz = np.zeros(v.shape, np.int64)
+    for _ in range(53):
+        z = ((v & 1) == 0) & nz
+        tz += z
+        v = np.where(z, v >> 1, v)
+    return np.where(nz, e - 53 + tz, 1 << 20)
+
+
+def probe_exact_condition(A: np.ndarray, B: np.ndarray) -> np.ndarray:
+    """Per output of A B^T (decoded operands, fp64): whether in every 64-wide
+    slice all products A[i, k] B[j, k] are integer multiples of a common 2^g
+    and their absolute sum is below 2^(g + 24), the condition under which
+    the probe-matched mode's slice sums are exact on the matrix core and its
+    outputs equal the oracle's bit for bit."""
+    la, lb = lsb_exp(A), lsb_exp(B)
+    ok = np.ones((A.shape[0], B.shape[0]), bool)
+    for s0 in range(0, A.shape[1], 64):
+        g = (la[:, None, s0:s0 + 64] + lb[None, :, s0:s0 + 64]).min(axis=2)
+        tot = np.abs(A[:, s0:s0 + 64]) @ np.abs(B[:, s0:s0 + 64]).T
+        ok &= (tot == 0) | (tot < np.ldexp(1.0, np.minimum(g, 1000) + 24))
+    return ok

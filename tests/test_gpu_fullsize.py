@@ -23,7 +23,7 @@ import torch
 import oracle
 from fp4_block_scaled_fp4q_amd import api, inputs
 from parity_util import (DEV, check_gemm_elementwise, gemm_ref_and_bound, host_rows,
-                         oracle_quantize_par, sub_operand)
+                         oracle_quantize_par, probe_exact_condition, sub_operand)
 
 pytestmark = pytest.mark.gpu
 
@@ -216,3 +216,30 @@ def test_ffn_step_gemm_band(ffn_step, ffn_oracle, gemm, band):
         ref, bound = gemm_ref_and_bound(a, sub_operand(b, c0, BAND), y.dtype)
         got = y[:, c0:c0 + BAND]
     check_gemm_elementwise(got, ref, bound, f"{gemm} {band} band")
+
+
+def test_ffn_step_probe_band(ffn_step, ffn_oracle):
+    """The probe-matched forward GEMM on the step's K64 operands at the full
+    FFN shape (16384 x 14336 x 4096, 128 x 128 tiles) with the 1/1024 snap,
+    as the benchmark times it: a 32-row by 256-column block crossing tile
+    boundaries in both directions against the oracle's probe rule. Every
+    output whose slices meet the exactness condition equals the oracle bit
+    for bit; the rest stay within 1024 units in the last place."""
+    xq, wq = ffn_step["xq"], ffn_step["wq"]
+    y = torch.empty((xq.rows, wq.rows), dtype=torch.float32, device=DEV)
+    api.fp4q_linear_probe(xq, wq, y, 10)
+    torch.cuda.synchronize()
+    r0, c0 = 8192 - 16, 7168 - 128
+    got = y[r0:r0 + 32, c0:c0 + 256].cpu().numpy()
+    del y
+    a = sub_operand(ffn_oracle["xq"], r0, 32)
+    b = sub_operand(ffn_oracle["wq"], c0, 256)
+    ref = oracle.gemm_probe(a, b, 10)
+    ok = probe_exact_condition(oracle.decode_f64(a), oracle.decode_f64(b))
+    assert ok.mean() > 0.9, ok.mean()
+    eq = got.view(np.uint32) == ref.view(np.uint32)
+    assert eq[ok].all(), f"{int((~eq[ok]).sum())} outputs meeting the condition differ"
+    rest = ~ok & ~eq
+    if rest.any():
+        ulps = np.abs(got[rest].view(np.int32).astype(np.int64) - ref[rest].view(np.int32).astype(np.int64))
+        assert ulps.max() <= 1024

@@ -50,3 +50,27 @@ def test_elementwise_bound_admits_fp32_accumulation_and_rejects_a_planted_error(
     # a row band of a TILE operand keeps its tile scales
     sub = sub_operand(qb, 32, 32)
     np.testing.assert_array_equal(oracle.decode_f64(sub), oracle.decode_f64(qb)[32:64])
+
+
+def test_lsb_exp_and_probe_exact_condition():
+    """The lowest-set-bit exponent on known values, and the probe mode's
+    exactness condition on slices whose products do and do not fit 24 bits
+    above their common lowest bit."""
+    from parity_util import lsb_exp, probe_exact_condition
+    x = np.array([1.0, 0.75, 6.0, -0.5, 2.0 ** -30 * 3, 0.0])
+    assert list(lsb_exp(x)[:5]) == [0, -2, 1, -1, -30]
+    assert lsb_exp(x)[5] > 1000
+    K = 128
+    A = np.zeros((3, K))
+    B = np.zeros((1, K))
+    A[0, :2] = [1.0, 1.0]                  # products 1, 1: exact
+    A[1, :2] = [1.0, 2.0 ** -30]           # products 1 and 2^-30: 31 bits apart
+    A[2, 0], A[2, 64] = 1.0, 2.0 ** -30    # the same two products in different slices: exact
+    B[0, :] = 1.0
+    assert probe_exact_condition(A, B)[:, 0].tolist() == [True, False, True]
+    # the boundary: 1 + 2^-24 needs 25 bits above the lowest (not exact),
+    # 0.5 + 2^-24 and 1 + 2^-23 need 24 (exact)
+    A2 = np.zeros((1, 64))
+    for pair, want in (([1.0, 2.0 ** -24], False), ([0.5, 2.0 ** -24], True), ([1.0, 2.0 ** -23], True)):
+        A2[0, :2] = pair
+        assert probe_exact_condition(A2, np.ones((1, 64)))[0, 0] == want, pair

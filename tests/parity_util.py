@@ -110,7 +110,8 @@ def _workers() -> int:
 
 
 def oracle_quantize_par(x: np.ndarray, amax_held: float, layout: int, rnd: int = 0, T: float = 448.0,
-                        seed: int = 0, subseq: int = 0, transposed: bool = False, chunk: int = 512):
+                        seed: int = 0, subseq: int = 0, transposed: bool = False, chunk: int = 512,
+                        block: int = 16, scale_fmt: int = 0):
     """oracle.quantize of a large tensor, run as independent chunks on host
     threads (the oracle's C calls release the GIL). Under a held amax a ROW16
     (or TILE) row band and a COL16 column band depend on their own elements
@@ -127,7 +128,7 @@ def oracle_quantize_par(x: np.ndarray, amax_held: float, layout: int, rnd: int =
         part = np.ascontiguousarray(x[:, s:e] if col else x[s:e])
         origin = (0, s, cols) if col else (s, 0, cols)
         return oracle.quantize(part, amax_held, T, layout, rnd, seed, subseq, transposed=transposed,
-                               origin=origin)
+                               origin=origin, block=block, scale_fmt=scale_fmt)
 
     with ThreadPoolExecutor(_workers()) as ex:
         parts = list(ex.map(run, starts))
@@ -135,25 +136,28 @@ def oracle_quantize_par(x: np.ndarray, amax_held: float, layout: int, rnd: int =
     codes = np.concatenate([p.q.codes for p in parts], axis=0)
     if layout == oracle.TILE16:
         scales = np.concatenate([p.q.scales for p in parts], axis=0)
-        q = oracle.QTensor(codes, scales, S, rows, cols, oracle.TILE16)
+        q = oracle.QTensor(codes, scales, S, rows, cols, oracle.TILE16, block, scale_fmt)
         qt = None
         if transposed:
             qt = oracle.QTensor(np.concatenate([p.qt.codes for p in parts], axis=1),
                                 np.concatenate([p.qt.scales for p in parts], axis=1), S, cols, rows,
-                                oracle.TILE16)
+                                oracle.TILE16, block, scale_fmt)
         return q, qt
     scales = np.concatenate([p.q.scales for p in parts], axis=0)
     if col:
-        return oracle.QTensor(codes, scales, S, cols, rows, oracle.ROW16), None
-    return oracle.QTensor(codes, scales, S, rows, cols, oracle.ROW16), None
+        return oracle.QTensor(codes, scales, S, cols, rows, oracle.ROW16, block, scale_fmt), None
+    return oracle.QTensor(codes, scales, S, rows, cols, oracle.ROW16, block, scale_fmt), None
 
 
 def sub_operand(q: oracle.QTensor, r0: int, n: int) -> oracle.QTensor:
-    """Rows [r0, r0+n) of an oracle operand (n and r0 multiples of 16 for TILE)."""
+    """Rows [r0, r0+n) of an oracle operand (n and r0 multiples of the block
+    size for TILE)."""
     if q.layout == oracle.TILE16:
-        return oracle.QTensor(q.codes[r0:r0 + n], q.scales[r0 // 16:(r0 + n) // 16], q.S, n, q.cols,
-                              q.layout)
-    return oracle.QTensor(q.codes[r0:r0 + n], q.scales[r0:r0 + n], q.S, n, q.cols, q.layout)
+        b = q.block
+        return oracle.QTensor(q.codes[r0:r0 + n], q.scales[r0 // b:(r0 + n) // b], q.S, n, q.cols,
+                              q.layout, q.block, q.scale_fmt)
+    return oracle.QTensor(q.codes[r0:r0 + n], q.scales[r0:r0 + n], q.S, n, q.cols, q.layout, q.block,
+                          q.scale_fmt)
 
 
 def gemm_ref_and_bound(a: oracle.QTensor, b: oracle.QTensor, out: torch.dtype):

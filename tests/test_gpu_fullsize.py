@@ -243,3 +243,46 @@ def test_ffn_step_probe_band(ffn_step, ffn_oracle):
     if rest.any():
         ulps = np.abs(got[rest].view(np.int32).astype(np.int64) - ref[rest].view(np.int32).astype(np.int64))
         assert ulps.max() <= 1024
+
+
+# the block-32 and E4M3-scale variants as the benchmark times them
+VARIANTS = [(32, 0, "block32_ue5m3"), (16, 1, "block16_e4m3"), (32, 1, "block32_e4m3")]
+
+
+@pytest.mark.parametrize("block,fmt,tag", VARIANTS)
+def test_quantize_full_size_variants(block, fmt, tag):
+    """The quantize-only workload (8192x4096 bf16 ROW16 RNE, held amax,
+    row-major packing) in each variant: whole tensor."""
+    wl = inputs.make("quantize")
+    X = wl.tensors["X"]
+    held, held_o = held_pair(X)
+    q, _, _ = api.quantize(X.t.to(DEV), held, T, api.ROW16, api.RNE, block=block, scale_fmt=fmt)
+    o = oracle.quantize(X.oracle_view, held_o, T, oracle.ROW16, block=block, scale_fmt=fmt)
+    check_q(q, o.q, f"X ROW16 {tag}")
+
+
+@pytest.mark.parametrize("block,fmt,tag", VARIANTS)
+def test_ffn_step_variant_fwd_band(ffn_step, block, fmt, tag):
+    """The forward GEMM of the FFN shape on variant operands (X ROW16 and W
+    TILE, K64 packing, the step's refresh maxima): W whole and the last 256
+    output rows, every element within the elementwise bound."""
+    wl = ffn_step["wl"]
+    X, W = wl.tensors["X"], wl.tensors["W"]
+    am = ffn_step["amax"]
+    xv, _, _ = api.quantize(X.t.to(DEV), am["X"], T, api.ROW16, block=block, scale_fmt=fmt, pack=api.PACK_K64)
+    wv, _, _ = api.quantize(W.t.to(DEV), am["W"], T, api.TILE16x16, block=block, scale_fmt=fmt,
+                            pack=api.PACK_K64)
+    M, N = xv.rows, wv.rows
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+    api.fp4q_linear_fwd(xv, wv, y)
+    torch.cuda.synchronize()
+    r0 = M - BAND
+    got = y[r0:r0 + BAND].clone()
+    del y, xv
+    ax, aw = float(npy(am["X"])[0]), float(npy(am["W"])[0])
+    ow, _ = oracle_quantize_par(W.oracle_view, aw, oracle.TILE16, block=block, scale_fmt=fmt)
+    check_q(wv, ow, f"W TILE {tag}")
+    ox = oracle.quantize(np.ascontiguousarray(X.oracle_view[r0:r0 + BAND]), ax, T, oracle.ROW16, block=block,
+                         scale_fmt=fmt).q
+    ref, bound = gemm_ref_and_bound(ox, ow, got.dtype)
+    check_gemm_elementwise(got, ref, bound, f"fwd {tag}, last {BAND} rows")

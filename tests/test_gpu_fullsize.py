@@ -286,3 +286,36 @@ def test_ffn_step_variant_fwd_band(ffn_step, block, fmt, tag):
                          scale_fmt=fmt).q
     ref, bound = gemm_ref_and_bound(ox, ow, got.dtype)
     check_gemm_elementwise(got, ref, bound, f"fwd {tag}, last {BAND} rows")
+
+
+def test_ffn_step_fp4linear_bands(ffn_step, ffn_oracle):
+    """The FP4Linear module's refresh step (step 0: fp32 master weight,
+    bf16 activations, seed 0) on the FFN shape, as the benchmark runs it,
+    against the oracle's quantizations of the same tensors (each under its
+    own maximum; dY with Philox seed 0, subsequence 0): the last 256 rows of
+    the output, of dX and of dW, every element within the elementwise
+    bound."""
+    from fp4_block_scaled_fp4q_amd.recipe import FP4Linear, Fp4Recipe
+    wl = ffn_step["wl"]
+    X, W, dY = (wl.tensors[k].t for k in ("X", "W", "dY"))
+    M, K = X.shape
+    N = W.shape[0]
+    layer = FP4Linear(K, N, Fp4Recipe(refresh_period=50), device=DEV)
+    with torch.no_grad():
+        layer.weight.copy_(W.to(DEV).float())
+    xin = X.to(DEV).requires_grad_(True)
+    y = layer(xin)
+    y.backward(dY.to(DEV))
+    torch.cuda.synchronize()
+    o = ffn_oracle
+    got = {"y": y.detach()[M - BAND:].clone(), "dx": xin.grad[M - BAND:].clone(),
+           "dw": layer.weight.grad[N - BAND:].clone()}
+    del layer, xin, y
+    torch.cuda.empty_cache()
+    cases = {"y": (sub_operand(o["xq"], M - BAND, BAND), o["wq"]),
+             "dx": (sub_operand(o["dyq"], M - BAND, BAND), o["wqt"]),
+             "dw": (sub_operand(o["dyqt"], N - BAND, BAND), o["xqt"])}
+    for k, (a, b) in cases.items():
+        ref, bound = gemm_ref_and_bound(a, b, got[k].dtype)
+        check_gemm_elementwise(got[k], ref, bound, f"FP4Linear {k}, last {BAND} rows")
+    assert got["dw"].dtype == torch.float32 and got["dx"].dtype == torch.bfloat16

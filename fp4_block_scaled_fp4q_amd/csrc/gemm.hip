@@ -6,7 +6,9 @@
 // Each decoded element e2m1 * dec has at most 6 significant bits and lies in
 // [2^-18, 368640]. The default accumulation decodes it times 2^-5, which is
 // exact in binary16 (at most 11520, a multiple of 2^-23), and contracts on
-// v_mfma_f32_32x32x16_f16 with fp32 accumulation; alpha absorbs the 2^10.
+// v_mfma_f32_16x16x32_f16 (v_mfma_f32_32x32x16_f16 where K % 64 != 0 or the
+// formats are not the default) with fp32 accumulation; alpha absorbs the
+// 2^10.
 // The probe-matched mode uses the same binary16 operands (each of its
 // 64-wide slice sums, their toward-zero additions and its snap then see
 // the values times 2^-10 exactly: no rounding step here depends on a power
@@ -15,26 +17,36 @@
 //
 // Design (gfx950):
 //  * A workgroup owns a 256 x 256 output tile; its 8 waves (2 along M x 4
-//    along N, two per SIMD) own 128 x 64 sub-tiles (8 MFMA accumulators of
-//    32 x 32 each).
+//    along N, two per SIMD) own 128 x 64 sub-tiles (32 MFMA accumulators of
+//    16 x 16, or 8 of 32 x 32).
+//  * 16 x 16 x 32 MFMAs: the chip runs these GEMMs power-limited, and on
+//    the decoded FP4 operands the 16 x 16 x 32 instruction sustains a much
+//    higher rate than 32 x 32 x 16 at the same nominal peak (a probe with
+//    register-resident operands: 0.94 against 0.78 of it). With it the
+//    GEMMs run at a higher clock; its k loop (16 MFMA groups per k tile,
+//    fragments read several groups ahead) is described at gemm_tile.
 //  * K advances in tiles of 64. FP4 codes (0.5 B/element) and one scale byte
 //    per 16 elements are read from global memory two tiles ahead into
 //    registers; every thread decodes one 64-element row of the stacked
 //    [A tile; B tile] into LDS, double buffered, in pieces placed between
 //    the MFMAs that consume the other buffer. Decoding once per workgroup
 //    costs (256 + 256) * 64 elements per 256 * 256 * 64 MACs.
-//  * The k tile is rotated: the decode ends with the third of its four k16
-//    steps, the workgroup barrier (LDS traffic only, so the codes in flight
-//    for later tiles are not waited for) comes before the fourth, and the
-//    next tile's first fragments are read under the fourth step's MFMAs.
+//  * The k tile is rotated: the decode ends before the last quarter of the
+//    tile's MFMAs, the workgroup barrier (LDS traffic only, so the codes in
+//    flight for later tiles are not waited for) comes there, and the next
+//    tile's first fragments are read under that quarter's MFMAs.
 //  * Decode: v_cvt_scalef32_pk_f16_fp4 (scale 1.0) gives two exact E2M1
 //    values as halves and one packed half multiply by the block's scale pair
 //    forms the products: two instructions per pair of elements. (A bf16
 //    decode, kept for FP4Q_PROBE_F16=0, takes four: a conversion to fp32,
 //    two fp32 multiplies and a packing conversion.)
-//  * LDS rows are 8 chunks of 16 bytes (8 k each) at a 144-byte pitch, so
-//    any 16 consecutive rows fall on distinct banks for the fragment reads
-//    (32 rows, one chunk) and the row-wise decode writes.
+//  * LDS rows are 8 chunks of 16 bytes (8 k each). The 16 x 16 kernels store
+//    them chunk-major (chunk c of row r at slot c * rows + r): their
+//    fragment reads (16 rows in each of 4 chunks) and the decode writes (64
+//    rows, one chunk) then touch consecutive slots and measured free of bank
+//    conflicts, where the 144-byte row pitch gave about 4 conflict cycles
+//    per fragment read. The 32 x 32 kernels keep the 144-byte pitch (their
+//    32-row reads are conflict-free with it, and it measured faster).
 //  * Workgroups are numbered so that consecutive ones on one XCD (hardware
 //    dispatch is round-robin over the 8 XCDs) cover a compact group of tiles,
 //    which keeps their shared A and B rows in that XCD's L2.
@@ -49,23 +61,49 @@
 // B = W^T, TILE) and wgrad (A = dY^T, B = X^T, both quantized along tokens):
 // both operands are stored contiguous along the contraction.
 #include <atomic>
+#include <type_traits>
 
 #include "codec.h"
 #include "kernels.h"
 
 // Build switches, defaults measured fastest. FP4Q_GEMM_SWZ: LDS layout of
-// the decoded tiles (2: 144-byte padded row pitch; 0 and 1: 128-byte rows
-// with the 16-byte chunk index XORed by row bits). FP4Q_GEMM_ROTATE: the
-// rotated k tile described above (0: decode, barrier, then all four k16
-// steps). FP4Q_PROBE_F16: binary16 operands in the probe-matched mode.
+// the default kernels' decoded tiles (3: chunk-major, the 16-byte chunk c of
+// row r at c * rows + r; 2: 144-byte padded row pitch; 0 and 1: 128-byte
+// rows with the chunk index XORed by row bits; the probe kernels use 2).
+// FP4Q_GEMM_ROTATE: the rotated k tile described above (0: decode,
+// barrier, then all four k16 steps). FP4Q_PROBE_F16: binary16 operands in
+// the probe-matched mode. FP4Q_GEMM_MFMA16: 16 x 16 x 32 MFMAs in the
+// default kernels (0: 32 x 32 x 16), scheduled by FP4Q_M16_TAIL (groups
+// after the barrier), FP4Q_M16_DIST (A fragments read this many groups
+// ahead), FP4Q_M16_BSTART (group reading the first B fragment of the
+// second k32 step) and FP4Q_M16_DEC0 / FP4Q_M16_DECSPAN (groups followed
+// by the decode pieces; span 0: up to the barrier).
 #ifndef FP4Q_GEMM_SWZ
-#define FP4Q_GEMM_SWZ 2
+#define FP4Q_GEMM_SWZ 3
 #endif
 #ifndef FP4Q_GEMM_ROTATE
 #define FP4Q_GEMM_ROTATE 1
 #endif
 #ifndef FP4Q_PROBE_F16
 #define FP4Q_PROBE_F16 1
+#endif
+#ifndef FP4Q_GEMM_MFMA16
+#define FP4Q_GEMM_MFMA16 1
+#endif
+#ifndef FP4Q_M16_TAIL
+#define FP4Q_M16_TAIL 4
+#endif
+#ifndef FP4Q_M16_DIST
+#define FP4Q_M16_DIST 5
+#endif
+#ifndef FP4Q_M16_BSTART
+#define FP4Q_M16_BSTART 3
+#endif
+#ifndef FP4Q_M16_DEC0
+#define FP4Q_M16_DEC0 0
+#endif
+#ifndef FP4Q_M16_DECSPAN
+#define FP4Q_M16_DECSPAN 0
 #endif
 
 namespace fp4q {
@@ -75,6 +113,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
@@ -269,9 +308,11 @@ __device__ __forceinline__ uint32_t seg_word(const RowSeg& g, int c) {
   }
 }
 
-// LDS slot of 16-byte chunk c of tile row r (8 chunks per 128-byte row).
-template <int kSwz>
+// LDS slot of 16-byte chunk c of tile row r (8 chunks per row of 64 k) in
+// a buffer of kRowsAll rows.
+template <int kSwz, int kRowsAll>
 __device__ __forceinline__ int slot(int r, int c) {
+  if (kSwz == 3) return c * kRowsAll + r;        // chunk-major
   if (kSwz == 2) return r * (kChunks + 1) + c;  // 144-byte row pitch
   return r * kChunks + (kSwz == 0 ? (c ^ (r & 7)) : (c ^ ((r >> 1) & 7)));
 }
@@ -291,8 +332,8 @@ __device__ __forceinline__ uint4* lds_base(uint4* arg) {
 }
 
 // One output tile: kWavesM x kWavesN waves over a kBM x kBN tile; wave
-// tile (kBM / kWavesM) x (kBN / kWavesN) built from 32 x 32 MFMA blocks. L
-// is the tile's logical workgroup index (see gemm_kernel below).
+// tile (kBM / kWavesM) x (kBN / kWavesN) built from 16 x 16 or 32 x 32 MFMA
+// blocks. L is the tile's logical workgroup index (see gemm_kernel below).
 //
 // kProbe: the probe-matched accumulation of the UE5M3 page (§6, Appendix
 // B). Each 64-wide k tile is one slice: its MFMAs start from zero, and the
@@ -317,8 +358,17 @@ __device__ __forceinline__ void gemm_tile(
   constexpr int kT = 64 * kWavesM * kWavesN;  // threads
   constexpr int kTM = kBM / kWavesM;           // wave tile rows
   constexpr int kTN = kBN / kWavesN;           // wave tile cols
-  constexpr int kFM = kTM / 32;               // MFMA blocks per wave along M
-  constexpr int kFN = kTN / 32;               // and along N
+  // default kernels with K % 64 == 0: 16 x 16 x 32 MFMA blocks; the
+  // others (general K, probe, format-generic): 32 x 32 x 16
+  constexpr bool kM16 = FP4Q_GEMM_MFMA16 && !kProbe && !kFmt && kFullK && FP4Q_GEMM_ROTATE;
+  constexpr int kEdge = kM16 ? 16 : 32;       // MFMA output block edge
+  constexpr int kAccN = kM16 ? 4 : 16;        // accumulators per lane and block
+  using acc_t = typename std::conditional<kM16, f32x4, f32x16>::type;
+  constexpr int kFM = kTM / kEdge;            // MFMA blocks per wave along M
+  // LDS layout: the chunk-major one (3) serves the 16 x 16 fragment reads
+  // without bank conflicts; the 32 x 32 path keeps the padded rows (2)
+  constexpr int kLay = (!kM16 && kSwz == 3) ? 2 : kSwz;
+  constexpr int kFN = kTN / kEdge;            // and along N
   constexpr int kRows = (kBM + kBN) / kT;       // A/B tile rows each thread decodes
   constexpr int kPieces = 2 * kRows;          // decode8 calls per thread per k16 step
   constexpr int kMfmaPerPiece = kFM * kFN / kPieces;
@@ -378,19 +428,19 @@ __device__ __forceinline__ void gemm_tile(
     const uint32_t code = seg_scale<kFmt>(g[i], s, is_a ? a_blk32 : b_blk32);
     const bool e4m3 = is_a ? a_e4m3 : b_e4m3;
     if constexpr (kF16)
-      buf[slot<kSwz>(q, c)] = decode8_h(seg_word(g[i], c), half_scale(code, e4m3));
+      buf[slot<kLay, kBM + kBN>(q, c)] = decode8_h(seg_word(g[i], c), half_scale(code, e4m3));
     else
-      buf[slot<kSwz>(q, c)] = decode8(seg_word(g[i], c), scale_value(code, e4m3));
+      buf[slot<kLay, kBM + kBN>(q, c)] = decode8(seg_word(g[i], c), scale_value(code, e4m3));
   };
 
-  f32x16 acc[kFM][kFN];
+  acc_t acc[kFM][kFN];
   f32x16 tot[kProbe ? kFM : 1][kProbe ? kFN : 1];  // running sums of the probe mode
 #pragma unroll
   for (int i = 0; i < kFM; ++i)
 #pragma unroll
     for (int j = 0; j < kFN; ++j)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+      for (int e = 0; e < kAccN; ++e) acc[i][j][e] = 0.0f;
 #pragma unroll
   for (int i = 0; i < (kProbe ? kFM : 1); ++i)
 #pragma unroll
@@ -413,94 +463,156 @@ __device__ __forceinline__ void gemm_tile(
     lds_barrier();  // the codes just requested are first needed by a decode of the first k tile
   }
 
-  const int arow0 = wm * kTM + (lane & 31);
-  const int brow0 = kBM + wn * kTN + (lane & 31);
-  const int hi = lane >> 5;
-
-  // fragments: eight 16-bit values per lane (binary16, or bf16 for a probe
-  // mode built with FP4Q_PROBE_F16=0), bit-cast to the MFMA's operand type
-  auto load_frags = [&](const uint4* buf, int s, bf16x8* af, bf16x8* bfr) {
-    const int ch = 2 * s + hi;
+  if constexpr (kM16) {
+    // 16 x 16 x 32 MFMAs (at the same nominal rate as 32 x 32 x 16, they
+    // move half the accumulator data per product and sustain a higher rate
+    // under the chip's power limit). A lane's fragment is 8 consecutive k of
+    // one row: row lane % 16 of the block, k chunk lane / 16 of the k32 step.
+    // A k tile is two k32 steps of kFM groups; group G multiplies A block
+    // row G % kFM with the step's kFN B fragments (4 MFMAs). The B
+    // fragments of a step stay in registers for it; A fragments are read two
+    // groups ahead. The next buffer's decode pieces follow groups spread over
+    // the first kG - 2 groups; the barrier (LDS traffic only) comes before
+    // the last two groups, whose fragments are in registers by then, and the
+    // next k tile's B fragments and first two A fragments are read from the
+    // freshly decoded buffer under those groups' MFMAs.
+    const int quad = lane >> 4;
+    const int arow = wm * kTM + (lane & 15);
+    const int brow = kBM + wn * kTN + (lane & 15);
+    constexpr int kG = 2 * kFM;  // A groups per k tile
+    constexpr int kTail = FP4Q_M16_TAIL;  // groups after the barrier
+    constexpr int kDist = FP4Q_M16_DIST;  // A fragments read this many groups ahead
+    constexpr int kBStart = FP4Q_M16_BSTART;  // group that reads the first B fragment of step 1
+    // decode pieces follow groups spread over [kDec0, kDec0 + kDecSpan)
+    constexpr int kDec0 = FP4Q_M16_DEC0;
+    constexpr int kDecSpan = FP4Q_M16_DECSPAN > 0 ? FP4Q_M16_DECSPAN : kG - kTail - kDec0;
+    static_assert(kDec0 + kDecSpan <= kG - kTail, "decode pieces precede the barrier");
+    static_assert(kFM >= kFN && kG - kTail >= 8 && kBStart + kFN <= kFM && kTail >= 2, "16 x 16 schedule: wave tile shape");
+    auto frag = [&](const uint4* buf, int row, int step) { return buf[slot<kLay, kBM + kBN>(row, 4 * step + quad)]; };
+    uint4 bq[2][kFN];  // B fragments of the k tile's two k32 steps
+    uint4 an[2];       // A fragments of the next k tile's first two groups
+    if (nk > k_begin) {
+      const uint4* b0 = lds_base<kLdsArg>(lds_arg);
 #pragma unroll
-    for (int i = 0; i < kFM; ++i) af[i] = __builtin_bit_cast(bf16x8, buf[slot<kSwz>(arow0 + 32 * i, ch)]);
+      for (int j = 0; j < kFN; ++j) bq[0][j] = frag(b0, brow + 16 * j, 0);
+      an[0] = frag(b0, arow, 0);
+      an[1] = frag(b0, arow + 16, 0);
+    }
+    auto k_step16 = [&](int kt, const RowSeg* gd, RowSeg* gl) {
+      constexpr int kBuf = (kBM + kBN) * row_pitch<kLay>();
+      const uint4* cur_buf = lds_base<kLdsArg>(lds_arg) + ((kt - k_begin) & 1) * kBuf;
+      uint4* next_buf = lds_base<kLdsArg>(lds_arg) + ((kt - k_begin + 1) & 1) * kBuf;
+      uint4 a[kG];
+      a[0] = an[0];
+      a[1] = an[1];
 #pragma unroll
-    for (int j = 0; j < kFN; ++j) bfr[j] = __builtin_bit_cast(bf16x8, buf[slot<kSwz>(brow0 + 32 * j, ch)]);
-  };
-
-  // one k tile: MFMAs on the current buffer while the codes of tile kt + 1
-  // (gd) are decoded into the other one and those of tile kt + 2 are loaded
-  // into gl. The loop runs two k tiles per trip with gd and gl swapping
-  // roles, so no register copy waits for the loads just issued, and the
-  // barrier between k tiles (lds_barrier) waits for LDS traffic only, not
-  // for the codes in flight for later k tiles.
-  // Fragments of the current and the next k16 step. With FP4Q_GEMM_ROTATE
-  // the decode of the next buffer ends with the third k16 step, the barrier
-  // comes before the fourth, and the next k tile's first fragments are read
-  // while the fourth step's MFMAs run (they are in registers when that k
-  // tile starts).
-  bf16x8 af[2][kFM], bfr[2][kFN];
-  if (FP4Q_GEMM_ROTATE && nk > k_begin) load_frags(lds_base<kLdsArg>(lds_arg), 0, af[0], bfr[0]);
-  constexpr int kMfma = kFM * kFN;                   // MFMAs per k16 step
-  constexpr int kDecStride = kMfma >= 8 ? kMfma / 4 : 1;
-  // the rotated schedule's 3 + 3 + 2 decode pieces: one tile row per thread
-  static_assert(!FP4Q_GEMM_ROTATE || (kRows == 1 && BK == 64), "rotated k tile: one decoded row per thread");
-  auto k_step = [&](int kt, const RowSeg* gd, RowSeg* gl) {
-    constexpr int kBuf = (kBM + kBN) * row_pitch<kSwz>();
-    const uint4* cur_buf = lds_base<kLdsArg>(lds_arg) + ((kt - k_begin) & 1) * kBuf;
-    uint4* next_buf = lds_base<kLdsArg>(lds_arg) + ((kt - k_begin + 1) & 1) * kBuf;
-    // codes of tile kt + 2 (the last tile again near the end: harmless);
-    // in the rotated default kernel they are requested after the first MFMA,
-    // so that their address arithmetic issues under it
-    constexpr bool kLateLoad = FP4Q_GEMM_ROTATE && !kProbe;
-    if (!kLateLoad) load_rows(gl, (int64_t)min(kt + 2, nk - 1) * BK);
-    if (!FP4Q_GEMM_ROTATE) load_frags(cur_buf, 0, af[0], bfr[0]);
+      for (int G = 0; G < kG; ++G) {
+        const int st = G / kFM, i = G % kFM;
+        if (G == kG - kTail) {
+          // every wave's decode into next_buf and its reads of cur_buf are done
+          lds_barrier();
 #pragma unroll
-    for (int s = 0; s < BK / 16; ++s) {
-      const int cb = s & 1;
-      if (s + 1 < BK / 16) {
-        load_frags(cur_buf, s + 1, af[cb ^ 1], bfr[cb ^ 1]);
-      } else if (FP4Q_GEMM_ROTATE) {
-        // every wave's decode into next_buf and its reads of this step's
-        // fragments are done: the next k tile's first fragments can be read
-        lds_barrier();
-        load_frags(next_buf, 0, af[cb ^ 1], bfr[cb ^ 1]);
-      }
-      if (FP4Q_GEMM_ROTATE) {
-        // the 2 * (BK / 16) decode pieces of the next buffer over the first
-        // three k16 steps (3, 3, 2), each after kDecStride MFMAs
-        constexpr int kQ = 2 * (BK / 16);
-        const int q0 = s == 0 ? 0 : s == 1 ? 3 : s == 2 ? 6 : kQ;
-        const int q1 = s == 0 ? 3 : s == 1 ? 6 : kQ;
+          for (int j = 0; j < kFN; ++j) bq[0][j] = frag(next_buf, brow + 16 * j, 0);
+          an[0] = frag(next_buf, arow, 0);
+          an[1] = frag(next_buf, arow + 16, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        // A fragment x (2 <= x < kG) is read at group min(max(x - kDist, 0),
+        // kG - kTail - 1): every read of cur_buf precedes the barrier
 #pragma unroll
-        for (int f = 0; f < kMfma; ++f) {
-          const int i = f / kFN, j = f % kFN;
-          if constexpr (kF16)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, af[cb][i]),
-                                                               __builtin_bit_cast(f16x8, bfr[cb][j]),
-                                                               (kProbe && s == 0) ? f32x16{} : acc[i][j], 0, 0, 0);
-          else
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                af[cb][i], bfr[cb][j], (kProbe && s == 0) ? f32x16{} : acc[i][j], 0, 0, 0);
-          const int q = q0 + f / kDecStride;
-          if ((f + 1) % kDecStride == 0 && q < q1) {
-            decode_piece(next_buf, gd, q >> 1, q & 1);
-            __builtin_amdgcn_sched_barrier(0);
-          }
-          if (kLateLoad && s == 0 && f == 0) {
+        for (int x = 2; x < kG; ++x)
+          if (min(max(x - kDist, 0), kG - kTail - 1) == G) a[x] = frag(cur_buf, arow + 16 * (x % kFM), x / kFM);
+        if (G >= kBStart && G < kBStart + kFN) bq[1][G - kBStart] = frag(cur_buf, brow + 16 * (G - kBStart), 1);
+#pragma unroll
+        for (int j = 0; j < kFN; ++j) {
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a[G]),
+                                                             __builtin_bit_cast(f16x8, bq[st][j]), acc[i][j], 0,
+                                                             0, 0);
+          if (G == 0 && j == 0) {
+            // codes of tile kt + 2 (the last tile again near the end: harmless)
             load_rows(gl, (int64_t)min(kt + 2, nk - 1) * BK);
             __builtin_amdgcn_sched_barrier(0);
           }
         }
+        // decode piece q (16-byte chunk q of this thread's row) follows
+        // group kDec0 + (q + 1) kDecSpan / 8 - 1
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+          if (kDec0 + (q + 1) * kDecSpan / 8 - 1 == G) {
+            decode_piece(next_buf, gd, q >> 1, q & 1);
+            __builtin_amdgcn_sched_barrier(0);
+          }
         __builtin_amdgcn_sched_barrier(0);
-      } else {
-        // block s of the next tile is decoded in kPieces pieces, each after
-        // kMfmaPerPiece MFMAs, so that the VALU work issues while the matrix
-        // core is busy
-#pragma unroll
-        for (int p = 0; p < kPieces; ++p) {
-#pragma unroll
-          for (int u = 0; u < kMfmaPerPiece; ++u) {
-            const int f = p * kMfmaPerPiece + u;
+      }
+    };
+    RowSeg g2[kRows];
+    int kt = k_begin;
+    for (; kt + 1 < nk; kt += 2) {
+      k_step16(kt, g, g2);
+      k_step16(kt + 1, g2, g);
+    }
+    if (kt < nk) k_step16(kt, g, g2);
+  } else {
+    const int arow0 = wm * kTM + (lane & 31);
+    const int brow0 = kBM + wn * kTN + (lane & 31);
+    const int hi = lane >> 5;
+
+    // fragments: eight 16-bit values per lane (binary16, or bf16 for a probe
+    // mode built with FP4Q_PROBE_F16=0), bit-cast to the MFMA's operand type
+    auto load_frags = [&](const uint4* buf, int s, bf16x8* af, bf16x8* bfr) {
+      const int ch = 2 * s + hi;
+  #pragma unroll
+      for (int i = 0; i < kFM; ++i) af[i] = __builtin_bit_cast(bf16x8, buf[slot<kLay, kBM + kBN>(arow0 + 32 * i, ch)]);
+  #pragma unroll
+      for (int j = 0; j < kFN; ++j) bfr[j] = __builtin_bit_cast(bf16x8, buf[slot<kLay, kBM + kBN>(brow0 + 32 * j, ch)]);
+    };
+
+    // one k tile: MFMAs on the current buffer while the codes of tile kt + 1
+    // (gd) are decoded into the other one and those of tile kt + 2 are loaded
+    // into gl. The loop runs two k tiles per trip with gd and gl swapping
+    // roles, so no register copy waits for the loads just issued, and the
+    // barrier between k tiles (lds_barrier) waits for LDS traffic only, not
+    // for the codes in flight for later k tiles.
+    // Fragments of the current and the next k16 step. With FP4Q_GEMM_ROTATE
+    // the decode of the next buffer ends with the third k16 step, the barrier
+    // comes before the fourth, and the next k tile's first fragments are read
+    // while the fourth step's MFMAs run (they are in registers when that k
+    // tile starts).
+    bf16x8 af[2][kFM], bfr[2][kFN];
+    if (FP4Q_GEMM_ROTATE && nk > k_begin) load_frags(lds_base<kLdsArg>(lds_arg), 0, af[0], bfr[0]);
+    constexpr int kMfma = kFM * kFN;                   // MFMAs per k16 step
+    constexpr int kDecStride = kMfma >= 8 ? kMfma / 4 : 1;
+    // the rotated schedule's 3 + 3 + 2 decode pieces: one tile row per thread
+    static_assert(!FP4Q_GEMM_ROTATE || (kRows == 1 && BK == 64), "rotated k tile: one decoded row per thread");
+    auto k_step = [&](int kt, const RowSeg* gd, RowSeg* gl) {
+      constexpr int kBuf = (kBM + kBN) * row_pitch<kLay>();
+      const uint4* cur_buf = lds_base<kLdsArg>(lds_arg) + ((kt - k_begin) & 1) * kBuf;
+      uint4* next_buf = lds_base<kLdsArg>(lds_arg) + ((kt - k_begin + 1) & 1) * kBuf;
+      // codes of tile kt + 2 (the last tile again near the end: harmless);
+      // in the rotated default kernel they are requested after the first MFMA,
+      // so that their address arithmetic issues under it
+      constexpr bool kLateLoad = FP4Q_GEMM_ROTATE && !kProbe;
+      if (!kLateLoad) load_rows(gl, (int64_t)min(kt + 2, nk - 1) * BK);
+      if (!FP4Q_GEMM_ROTATE) load_frags(cur_buf, 0, af[0], bfr[0]);
+  #pragma unroll
+      for (int s = 0; s < BK / 16; ++s) {
+        const int cb = s & 1;
+        if (s + 1 < BK / 16) {
+          load_frags(cur_buf, s + 1, af[cb ^ 1], bfr[cb ^ 1]);
+        } else if (FP4Q_GEMM_ROTATE) {
+          // every wave's decode into next_buf and its reads of this step's
+          // fragments are done: the next k tile's first fragments can be read
+          lds_barrier();
+          load_frags(next_buf, 0, af[cb ^ 1], bfr[cb ^ 1]);
+        }
+        if (FP4Q_GEMM_ROTATE) {
+          // the 2 * (BK / 16) decode pieces of the next buffer over the first
+          // three k16 steps (3, 3, 2), each after kDecStride MFMAs
+          constexpr int kQ = 2 * (BK / 16);
+          const int q0 = s == 0 ? 0 : s == 1 ? 3 : s == 2 ? 6 : kQ;
+          const int q1 = s == 0 ? 3 : s == 1 ? 6 : kQ;
+  #pragma unroll
+          for (int f = 0; f < kMfma; ++f) {
             const int i = f / kFN, j = f % kFN;
             if constexpr (kF16)
               acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, af[cb][i]),
@@ -509,49 +621,78 @@ __device__ __forceinline__ void gemm_tile(
             else
               acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                   af[cb][i], bfr[cb][j], (kProbe && s == 0) ? f32x16{} : acc[i][j], 0, 0, 0);
+            const int q = q0 + f / kDecStride;
+            if ((f + 1) % kDecStride == 0 && q < q1) {
+              decode_piece(next_buf, gd, q >> 1, q & 1);
+              __builtin_amdgcn_sched_barrier(0);
+            }
+            if (kLateLoad && s == 0 && f == 0) {
+              load_rows(gl, (int64_t)min(kt + 2, nk - 1) * BK);
+              __builtin_amdgcn_sched_barrier(0);
+            }
           }
-          decode_piece(next_buf, gd, s, p);
           __builtin_amdgcn_sched_barrier(0);
+        } else {
+          // block s of the next tile is decoded in kPieces pieces, each after
+          // kMfmaPerPiece MFMAs, so that the VALU work issues while the matrix
+          // core is busy
+  #pragma unroll
+          for (int p = 0; p < kPieces; ++p) {
+  #pragma unroll
+            for (int u = 0; u < kMfmaPerPiece; ++u) {
+              const int f = p * kMfmaPerPiece + u;
+              const int i = f / kFN, j = f % kFN;
+              if constexpr (kF16)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, af[cb][i]),
+                                                                   __builtin_bit_cast(f16x8, bfr[cb][j]),
+                                                                   (kProbe && s == 0) ? f32x16{} : acc[i][j], 0, 0, 0);
+              else
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    af[cb][i], bfr[cb][j], (kProbe && s == 0) ? f32x16{} : acc[i][j], 0, 0, 0);
+            }
+            decode_piece(next_buf, gd, s, p);
+            __builtin_amdgcn_sched_barrier(0);
+          }
         }
       }
+      if constexpr (kProbe) {
+        // add the slice partials to the running sums with round-toward-zero.
+        // The MODE rounding field governs these VALU additions only: MFMA
+        // results are the same under either mode (checked on 65536 random
+        // outputs). The compiler does not model the additions' dependence on
+        // MODE (a plain fp32 add may legally move across a MODE write, and
+        // one k tile's additions of each unrolled pair did), so the two MODE
+        // writes and every addition are volatile asm statements, which keep
+        // their order: all 64 additions run inside the window. The asm hides
+        // the additions' reads of the matrix core's results from the
+        // compiler's hazard tracking, so the window opens with 24 wait states
+        // (more than a 16-pass MFMA result needs before a VALU read, and the
+        // MODE write's own two).
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("s_setreg_imm32_b32 hwreg(HW_REG_MODE, 0, 2), 3\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+  #pragma unroll
+        for (int i = 0; i < kFM; ++i)
+  #pragma unroll
+          for (int j = 0; j < kFN; ++j)
+  #pragma unroll
+            for (int e = 0; e < 16; ++e) {
+              float t;
+              asm volatile("v_add_f32 %0, %1, %2" : "=v"(t) : "v"(tot[i][j][e]), "v"(acc[i][j][e]));
+              tot[i][j][e] = t;
+            }
+        asm volatile("s_setreg_imm32_b32 hwreg(HW_REG_MODE, 0, 2), 0\n\ts_nop 1" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (!FP4Q_GEMM_ROTATE) lds_barrier();
+    };
+    RowSeg g2[kRows];
+    int kt = k_begin;
+    for (; kt + 1 < nk; kt += 2) {
+      k_step(kt, g, g2);
+      k_step(kt + 1, g2, g);
     }
-    if constexpr (kProbe) {
-      // add the slice partials to the running sums with round-toward-zero.
-      // The MODE rounding field governs these VALU additions only: MFMA
-      // results are the same under either mode (checked on 65536 random
-      // outputs). The compiler does not model the additions' dependence on
-      // MODE (a plain fp32 add may legally move across a MODE write, and
-      // one k tile's additions of each unrolled pair did), so the two MODE
-      // writes and every addition are volatile asm statements, which keep
-      // their order: all 64 additions run inside the window. The asm hides
-      // the additions' reads of the matrix core's results from the
-      // compiler's hazard tracking, so the window opens with 24 wait states
-      // (more than a 16-pass MFMA result needs before a VALU read, and the
-      // MODE write's own two).
-      __builtin_amdgcn_sched_barrier(0);
-      asm volatile("s_setreg_imm32_b32 hwreg(HW_REG_MODE, 0, 2), 3\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
-#pragma unroll
-      for (int i = 0; i < kFM; ++i)
-#pragma unroll
-        for (int j = 0; j < kFN; ++j)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            float t;
-            asm volatile("v_add_f32 %0, %1, %2" : "=v"(t) : "v"(tot[i][j][e]), "v"(acc[i][j][e]));
-            tot[i][j][e] = t;
-          }
-      asm volatile("s_setreg_imm32_b32 hwreg(HW_REG_MODE, 0, 2), 0\n\ts_nop 1" ::: "memory");
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    if (!FP4Q_GEMM_ROTATE) lds_barrier();
-  };
-  RowSeg g2[kRows];
-  int kt = k_begin;
-  for (; kt + 1 < nk; kt += 2) {
-    k_step(kt, g, g2);
-    k_step(kt + 1, g2, g);
+    if (kt < nk) k_step(kt, g, g2);
   }
-  if (kt < nk) k_step(kt, g, g2);
   if constexpr (kProbe) {
     // sums of binary16 operands carry 2^-10 (alpha restores it): the snap
     // grid moves by the same 10 bits
@@ -577,6 +718,12 @@ __device__ __forceinline__ void gemm_tile(
   const float alpha = (float)alpha_d;
   const bool alpha_normal = alpha >= 1.17549435e-38f && alpha <= 3.40282347e+38f;
   constexpr int es = kF32Out ? 4 : 2;
+  // accumulator e of block (i, j): in-tile row i kEdge + erow(e) + lrow,
+  // column j kEdge + (lane % kEdge) (32 x 32 blocks: rows 8 (e / 4) + e % 4
+  // + 4 (lane / 32); 16 x 16 blocks: rows e + 4 (lane / 16))
+  const int lrow = kM16 ? 4 * (lane >> 4) : 4 * (lane >> 5);
+  const int lcol = lane & (kEdge - 1);
+  auto erow = [](int e) { return kM16 ? e : 8 * (e >> 2) + (e & 3); };
   if (kF32Out && half >= 0) {
     // one half of a split tile: add into the zeroed output (two additions
     // onto zero give the same sum in either order)
@@ -584,10 +731,10 @@ __device__ __forceinline__ void gemm_tile(
     for (int i = 0; i < kFM; ++i)
 #pragma unroll
       for (int j = 0; j < kFN; ++j) {
-        const int64_t c = n0 + wn * kTN + j * 32 + (lane & 31);
+        const int64_t c = n0 + wn * kTN + j * kEdge + lcol;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int64_t r = m0 + wm * kTM + i * 32 + 8 * (e >> 2) + 4 * hi + (e & 3);
+        for (int e = 0; e < kAccN; ++e) {
+          const int64_t r = m0 + wm * kTM + i * kEdge + erow(e) + lrow;
           const float v = alpha_normal ? acc[i][j][e] * alpha : (float)((double)acc[i][j][e] * alpha_d);
           if (r < M && c < N) unsafeAtomicAdd(static_cast<float*>(y) + r * N + c, v);
         }
@@ -597,15 +744,15 @@ __device__ __forceinline__ void gemm_tile(
   const bool full_tile = m0 + kBM <= M && n0 + kBN <= N;
   if (full_tile && alpha_normal && N * es * kBM < 0xFFFFFFFFll) {
     char* tile_base = static_cast<char*>(y) + (m0 * N + n0) * es;
-    const uint32_t lane_off = (uint32_t)(((wm * kTM + 4 * hi) * N + wn * kTN + (lane & 31)) * es);
+    const uint32_t lane_off = (uint32_t)(((wm * kTM + lrow) * N + wn * kTN + lcol) * es);
 #pragma unroll
     for (int i = 0; i < kFM; ++i)
 #pragma unroll
       for (int j = 0; j < kFN; ++j)
 #pragma unroll
-        for (int e = 0; e < 16; e += 2) {
-          const uint32_t r0 = (uint32_t)(i * 32 + 8 * (e >> 2) + (e & 3));
-          const uint32_t o0 = lane_off + (uint32_t)((r0 * N + j * 32) * es);
+        for (int e = 0; e < kAccN; e += 2) {
+          const uint32_t r0 = (uint32_t)(i * kEdge + erow(e));
+          const uint32_t o0 = lane_off + (uint32_t)((r0 * N + j * kEdge) * es);
           const uint32_t o1 = o0 + (uint32_t)(N * es);
           const float v0 = acc[i][j][e] * alpha, v1 = acc[i][j][e + 1] * alpha;
           if (kF32Out) {
@@ -622,10 +769,10 @@ __device__ __forceinline__ void gemm_tile(
   for (int i = 0; i < kFM; ++i)
 #pragma unroll
     for (int j = 0; j < kFN; ++j) {
-      const int64_t c = n0 + wn * kTN + j * 32 + (lane & 31);
+      const int64_t c = n0 + wn * kTN + j * kEdge + lcol;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int64_t r = m0 + wm * kTM + i * 32 + 8 * (e >> 2) + 4 * hi + (e & 3);
+      for (int e = 0; e < kAccN; ++e) {
+        const int64_t r = m0 + wm * kTM + i * kEdge + erow(e) + lrow;
         const float v = alpha_normal ? acc[i][j][e] * alpha : (float)((double)acc[i][j][e] * alpha_d);
         if (r < M && c < N) {
           if (kF32Out) {
@@ -763,7 +910,8 @@ hipError_t launch_kernel(const QOperand& a, const QOperand& b, void* y, int y_es
   const int tiles_m = (int)((M + kBM - 1) / kBM);
   const int tiles_n = (int)((N + kBN - 1) / kBN);
   const bool full_k = K % BK == 0;
-  const size_t lds_bytes = 2 * (kBM + kBN) * (kSW == 2 ? kChunks + 1 : kChunks) * sizeof(uint4);
+  // layouts 2 and 3 (whose 32 x 32 kernels use 2) take the padded size
+  const size_t lds_bytes = 2 * (kBM + kBN) * (kSW >= 2 ? kChunks + 1 : kChunks) * sizeof(uint4);
   const void* fn;
   if (k64)
     fn = y_es == 4 ? (const void*)gemm_kernel<kBM, kBN, true, true, kWM, kWN, kSW, kProbe, kFmt, true>

@@ -469,11 +469,12 @@ __device__ __forceinline__ void gemm_tile(
     // under the chip's power limit). A lane's fragment is 8 consecutive k of
     // one row: row lane % 16 of the block, k chunk lane / 16 of the k32 step.
     // A k tile is two k32 steps of kFM groups; group G multiplies A block
-    // row G % kFM with the step's kFN B fragments (4 MFMAs). The B
-    // fragments of a step stay in registers for it; A fragments are read two
-    // groups ahead. The next buffer's decode pieces follow groups spread over
-    // the first kG - 2 groups; the barrier (LDS traffic only) comes before
-    // the last two groups, whose fragments are in registers by then, and the
+    // row G % kFM with the step's kFN B fragments (kFN MFMAs). The B
+    // fragments of a step stay in registers for it (the second step's are
+    // read from group kBStart on); A fragments are read kDist groups ahead.
+    // The next buffer's decode pieces follow groups spread over the first
+    // kG - kTail groups; the barrier (LDS traffic only) comes before the
+    // last kTail groups, whose fragments are in registers by then, and the
     // next k tile's B fragments and first two A fragments are read from the
     // freshly decoded buffer under those groups' MFMAs.
     const int quad = lane >> 4;
@@ -487,8 +488,11 @@ __device__ __forceinline__ void gemm_tile(
     constexpr int kDec0 = FP4Q_M16_DEC0;
     constexpr int kDecSpan = FP4Q_M16_DECSPAN > 0 ? FP4Q_M16_DECSPAN : kG - kTail - kDec0;
     static_assert(kDec0 + kDecSpan <= kG - kTail, "decode pieces precede the barrier");
-    static_assert(kFM >= kFN && kG - kTail >= 8 && kBStart + kFN <= kFM && kTail >= 2, "16 x 16 schedule: wave tile shape");
-    auto frag = [&](const uint4* buf, int row, int step) { return buf[slot<kLay, kBM + kBN>(row, 4 * step + quad)]; };
+    static_assert(kFM >= kFN && kG - kTail >= 8 && kBStart + kFN <= kFM && kTail >= 2,
+                  "16 x 16 schedule: wave tile shape");
+    auto frag = [&](const uint4* buf, int row, int step) {
+      return buf[slot<kLay, kBM + kBN>(row, 4 * step + quad)];
+    };
     uint4 bq[2][kFN];  // B fragments of the k tile's two k32 steps
     uint4 an[2];       // A fragments of the next k tile's first two groups
     if (nk > k_begin) {
@@ -521,8 +525,10 @@ __device__ __forceinline__ void gemm_tile(
         // kG - kTail - 1): every read of cur_buf precedes the barrier
 #pragma unroll
         for (int x = 2; x < kG; ++x)
-          if (min(max(x - kDist, 0), kG - kTail - 1) == G) a[x] = frag(cur_buf, arow + 16 * (x % kFM), x / kFM);
-        if (G >= kBStart && G < kBStart + kFN) bq[1][G - kBStart] = frag(cur_buf, brow + 16 * (G - kBStart), 1);
+          if (min(max(x - kDist, 0), kG - kTail - 1) == G)
+            a[x] = frag(cur_buf, arow + 16 * (x % kFM), x / kFM);
+        if (G >= kBStart && G < kBStart + kFN)
+          bq[1][G - kBStart] = frag(cur_buf, brow + 16 * (G - kBStart), 1);
 #pragma unroll
         for (int j = 0; j < kFN; ++j) {
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a[G]),
@@ -561,10 +567,12 @@ __device__ __forceinline__ void gemm_tile(
     // mode built with FP4Q_PROBE_F16=0), bit-cast to the MFMA's operand type
     auto load_frags = [&](const uint4* buf, int s, bf16x8* af, bf16x8* bfr) {
       const int ch = 2 * s + hi;
-  #pragma unroll
-      for (int i = 0; i < kFM; ++i) af[i] = __builtin_bit_cast(bf16x8, buf[slot<kLay, kBM + kBN>(arow0 + 32 * i, ch)]);
-  #pragma unroll
-      for (int j = 0; j < kFN; ++j) bfr[j] = __builtin_bit_cast(bf16x8, buf[slot<kLay, kBM + kBN>(brow0 + 32 * j, ch)]);
+#pragma unroll
+      for (int i = 0; i < kFM; ++i)
+        af[i] = __builtin_bit_cast(bf16x8, buf[slot<kLay, kBM + kBN>(arow0 + 32 * i, ch)]);
+#pragma unroll
+      for (int j = 0; j < kFN; ++j)
+        bfr[j] = __builtin_bit_cast(bf16x8, buf[slot<kLay, kBM + kBN>(brow0 + 32 * j, ch)]);
     };
 
     // one k tile: MFMAs on the current buffer while the codes of tile kt + 1
@@ -594,7 +602,7 @@ __device__ __forceinline__ void gemm_tile(
       constexpr bool kLateLoad = FP4Q_GEMM_ROTATE && !kProbe;
       if (!kLateLoad) load_rows(gl, (int64_t)min(kt + 2, nk - 1) * BK);
       if (!FP4Q_GEMM_ROTATE) load_frags(cur_buf, 0, af[0], bfr[0]);
-  #pragma unroll
+#pragma unroll
       for (int s = 0; s < BK / 16; ++s) {
         const int cb = s & 1;
         if (s + 1 < BK / 16) {
@@ -611,13 +619,13 @@ __device__ __forceinline__ void gemm_tile(
           constexpr int kQ = 2 * (BK / 16);
           const int q0 = s == 0 ? 0 : s == 1 ? 3 : s == 2 ? 6 : kQ;
           const int q1 = s == 0 ? 3 : s == 1 ? 6 : kQ;
-  #pragma unroll
+#pragma unroll
           for (int f = 0; f < kMfma; ++f) {
             const int i = f / kFN, j = f % kFN;
             if constexpr (kF16)
-              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, af[cb][i]),
-                                                                 __builtin_bit_cast(f16x8, bfr[cb][j]),
-                                                                 (kProbe && s == 0) ? f32x16{} : acc[i][j], 0, 0, 0);
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                  __builtin_bit_cast(f16x8, af[cb][i]), __builtin_bit_cast(f16x8, bfr[cb][j]),
+                  (kProbe && s == 0) ? f32x16{} : acc[i][j], 0, 0, 0);
             else
               acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                   af[cb][i], bfr[cb][j], (kProbe && s == 0) ? f32x16{} : acc[i][j], 0, 0, 0);
@@ -636,16 +644,16 @@ __device__ __forceinline__ void gemm_tile(
           // block s of the next tile is decoded in kPieces pieces, each after
           // kMfmaPerPiece MFMAs, so that the VALU work issues while the matrix
           // core is busy
-  #pragma unroll
+#pragma unroll
           for (int p = 0; p < kPieces; ++p) {
-  #pragma unroll
+#pragma unroll
             for (int u = 0; u < kMfmaPerPiece; ++u) {
               const int f = p * kMfmaPerPiece + u;
               const int i = f / kFN, j = f % kFN;
               if constexpr (kF16)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, af[cb][i]),
-                                                                   __builtin_bit_cast(f16x8, bfr[cb][j]),
-                                                                   (kProbe && s == 0) ? f32x16{} : acc[i][j], 0, 0, 0);
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                    __builtin_bit_cast(f16x8, af[cb][i]), __builtin_bit_cast(f16x8, bfr[cb][j]),
+                    (kProbe && s == 0) ? f32x16{} : acc[i][j], 0, 0, 0);
               else
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                     af[cb][i], bfr[cb][j], (kProbe && s == 0) ? f32x16{} : acc[i][j], 0, 0, 0);
@@ -669,12 +677,13 @@ __device__ __forceinline__ void gemm_tile(
         // (more than a 16-pass MFMA result needs before a VALU read, and the
         // MODE write's own two).
         __builtin_amdgcn_sched_barrier(0);
-        asm volatile("s_setreg_imm32_b32 hwreg(HW_REG_MODE, 0, 2), 3\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
-  #pragma unroll
+        asm volatile("s_setreg_imm32_b32 hwreg(HW_REG_MODE, 0, 2), 3\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::
+                         : "memory");
+#pragma unroll
         for (int i = 0; i < kFM; ++i)
-  #pragma unroll
+#pragma unroll
           for (int j = 0; j < kFN; ++j)
-  #pragma unroll
+#pragma unroll
             for (int e = 0; e < 16; ++e) {
               float t;
               asm volatile("v_add_f32 %0, %1, %2" : "=v"(t) : "v"(tot[i][j][e]), "v"(acc[i][j][e]));

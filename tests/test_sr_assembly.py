@@ -14,7 +14,8 @@ in the device assembly of quantize.hip built with the package's own flags
   lowest is followed by a wait state (as the compiler schedules the
   round-to-nearest form of the same chain).
 - The round-to-nearest kernels hold no MODE write and no stochastic
-  conversion."""
+  conversion.
+- No quantize kernel spills registers."""
 import os
 import re
 import subprocess
@@ -48,7 +49,10 @@ def test_sr_windows_and_conversion_chains(tmp_path):
     cmd = [build.HIPCC, *build.FLAGS, "--cuda-device-only", "-S", os.path.join(build.CSRC, "quantize.hip"), "-o", out]
     r = subprocess.run(cmd, capture_output=True, text=True)
     assert r.returncode == 0, r.stderr[-2000:]
-    lines = open(out).read().split("\n")
+    text = open(out).read()
+    lines = text.split("\n")
+    spills = re.findall(r"\.vgpr_spill_count:\s+(\d+)", text)
+    assert spills and all(c == "0" for c in spills), spills
     sr_kernels = rne_kernels = 0
     for name, body in _kernels(lines, r"quant_(row|dual|tile|tile32)_kernel"):
         # template arguments <kBF16, kSR, ...>: the second is kSR

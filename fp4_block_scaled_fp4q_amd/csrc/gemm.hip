@@ -52,7 +52,8 @@
 //    which keeps their shared A and B rows in that XCD's L2.
 //  * A workgroup of the default kernels runs two tiles of that order one
 //    after the other where the chip's tile rounds stay as many (fwd, dgrad
-//    and wgrad of the FFN shapes): 0.3-0.8% faster steps.
+//    and wgrad of the FFN shapes): 0.3-0.8% faster steps with 32 x 32 x 16
+//    MFMAs, the same with 16 x 16 x 32.
 //  * Under sustained load the chip runs power-limited (its clock drops well
 //    below the nominal 2.4 GHz); the binary16 decode's fewer VALU
 //    instructions measured about 4% faster than the bf16 decode.
